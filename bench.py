@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark one GPU's share of ring attention on an MI355X.
+
+A step is one full pass of the shard: the local Q rows attend to every K/V
+chunk and the float32 output + LSE are produced (``ringattn_forward``: all
+chunk passes, the LSE merge and, if planned, the split merge).  Inputs are
+seeded synthetic bf16 tensors already resident in HBM when timing starts.
+
+Prints ONE JSON line.  ``value`` is attention TFLOP/s = 4*B*Sq*Skv*D*H /
+seconds per step.  ``roofline`` reports the attention kernel against the
+published MI355X dense bf16 MFMA peak (2.5 PFLOP/s), with its duration taken
+from HIP events on the stream the kernel is launched on.  ``cpu_baseline``
+times the fp64 oracle on a bounded sample of query rows on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (4·Sq·Skv·D·H) per ring shard on 1 MI355X; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video",
+                    help="tiny | flux | ring_anything | ulysses | video (default: video)")
+    ap.add_argument("--splits", type=int, default=0, help="force the K/V split count (0 = library plan)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate host time spent timing the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch of the attention kernel from committed rocprofv3
+    PMC summaries (profiles/<kernel>_<workload>_traffic.json), or None."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(x, target_s: float):
+    """Time the oracle on a sample of local query rows (all heads, all keys)."""
+    import numpy as np
+
+    import oracle
+    from context_attention_diffusion_ringattn_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing or no BLAS info
+        threads = 1
+    w = x["workload"]
+    q64, k64, v64 = W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"])
+    rng = np.random.default_rng(1234)
+
+    def run(n):
+        rows = sorted(int(r) for r in rng.choice(w.q_rows, size=min(n, w.q_rows), replace=False))
+        t0 = time.perf_counter()
+        out, lse = oracle.attention_rows_fp64(q64, k64, v64, x["scale"], rows)
+        return rows, out, lse, time.perf_counter() - t0
+
+    n0 = min(4, w.q_rows)
+    _, _, _, t0 = run(n0)
+    n = int(max(n0, min(w.q_rows, n0 * target_s / max(t0, 1e-3))))
+    rows, out, lse, t = run(n)
+    flops = 4.0 * w.batch * len(rows) * w.seq_len * w.head_dim * w.heads
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {w.q_rows} local query rows x {w.heads} heads x {w.seq_len} keys "
+                  f"(fp64 NumPy, {t:.1f} s)",
+    }, rows, out, lse
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's ring shard only; this build has no multi-GPU path "
+              "(the K/V exchange between GPUs is not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import context_attention_diffusion_ringattn_amd as ra
+    from context_attention_diffusion_ringattn_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    x = W.make_inputs(args.workload)
+    w = x["workload"]
+    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    offs = ra.chunk_offsets(w.seq_len, w.n_chunks, w.ring_anything)
+    n_splits, ws_bytes = ra.forward_plan(tuple(q.shape), offs, args.splits)
+    out = torch.empty((w.batch, w.q_rows, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.heads, w.q_rows), dtype=torch.float32, device=dev)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+
+    def step():
+        ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=args.splits, out=out, lse=lse,
+                   workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1e3 / args.steps
+    avg_ms = float(np.mean(per_launch_ms))
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+
+    traffic = traffic_from_profiles(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+            "q_rows": w.q_rows, "kv_rows": w.seq_len, "n_chunks": w.n_chunks,
+            "ring_anything": w.ring_anything,
+            "flops_per_step": flops,
+            "splits": n_splits,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms": {"mean": round(avg_ms, 4), "median": round(float(np.median(per_launch_ms)), 4),
+                          "min": round(float(np.min(per_launch_ms)), 4)},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cb, rows, ref_out, ref_lse = cpu_baseline(x, args.cpu_seconds)
+        result["cpu_baseline"] = cb
+        o = out[:, rows].detach().cpu().double().numpy()
+        l = lse[:, :, rows].detach().cpu().double().numpy()
+        result["parity"] = {"rows_checked": len(rows),
+                            "max_abs_err_out": float(np.max(np.abs(o - ref_out))),
+                            "max_abs_err_lse": float(np.max(np.abs(l - ref_lse)))}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

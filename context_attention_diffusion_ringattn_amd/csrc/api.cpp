@@ -1,0 +1,357 @@
+// api.cpp -- the C ABI of include/ringattn.h: argument validation, the chunk
+// partition, launch planning and kernel launches.  Validation always runs
+// before any HIP call, so every error path works on a machine with no GPU.
+#include "ringattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace ringattn;
+
+static_assert(kMaxChunks == RINGATTN_MAX_CHUNKS, "chunk limit mismatch");
+
+constexpr int32_t kAbiVersion = 1;
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return RINGATTN_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_hip(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(RINGATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape checks shared by every entry point.  `kv_matters` is false where
+// shape->kv_len is ignored.
+int check_shape(const ringattn_shape *s, bool kv_matters) {
+    if (!s) return fail(RINGATTN_EINVAL, "shape is NULL");
+    if (s->reserved != 0) return fail(RINGATTN_EINVAL, "shape.reserved must be 0");
+    if (s->batch < 1) return fail(RINGATTN_EINVAL, "batch must be >= 1 (got %d)", s->batch);
+    if (s->heads < 1) return fail(RINGATTN_EINVAL, "heads must be >= 1 (got %d)", s->heads);
+    if (s->q_len < 1) return fail(RINGATTN_EINVAL, "q_len must be >= 1 (got %lld)", (long long)s->q_len);
+    if (kv_matters && s->kv_len < 0) return fail(RINGATTN_EINVAL, "kv_len must be >= 0");
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return fail(RINGATTN_EUNSUPPORTED, "head_dim %d not built (64 or 128)", s->head_dim);
+    // every element index must fit comfortably in int64 and grid sizes in int32
+    const double elems = (double)s->batch * (double)s->q_len * s->heads * s->head_dim;
+    if (elems > 4.0e18) return fail(RINGATTN_EINVAL, "tensor too large");
+    return RINGATTN_OK;
+}
+
+int check_ptr(const void *p, uintptr_t align, const char *name) {
+    if (!p) return fail(RINGATTN_EINVAL, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(RINGATTN_EINVAL, "%s is not %u-byte aligned", name, (unsigned)align);
+    return RINGATTN_OK;
+}
+
+int cu_count_for_current_device() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;  // MI355X
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+// Fill the chunk table from host offsets; validates the offsets.
+int build_chunk_table(const int64_t *offsets, int32_t n_chunks, int64_t stride, int64_t kv_len, ChunkTable *ct,
+                      int64_t *kv_rows) {
+    if (!offsets) return fail(RINGATTN_EINVAL, "chunk_offsets is NULL");
+    if (n_chunks < 1 || n_chunks > kMaxChunks)
+        return fail(RINGATTN_EINVAL, "n_chunks %d outside [1, %d]", n_chunks, kMaxChunks);
+    if (stride < 0) return fail(RINGATTN_EINVAL, "kv_chunk_stride must be >= 0");
+    if (offsets[0] != 0) return fail(RINGATTN_EINVAL, "chunk_offsets[0] must be 0");
+    if (offsets[n_chunks] != kv_len)
+        return fail(RINGATTN_EINVAL, "chunk_offsets[%d] = %lld must equal kv_len %lld", n_chunks,
+                    (long long)offsets[n_chunks], (long long)kv_len);
+    std::memset(ct, 0, sizeof *ct);
+    ct->n_chunks = n_chunks;
+    int64_t tiles = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t len = offsets[c + 1] - offsets[c];
+        if (len < 0) return fail(RINGATTN_EINVAL, "chunk_offsets decrease at %d", c);
+        if (stride > 0 && len > stride)
+            return fail(RINGATTN_EINVAL, "chunk %d length %lld exceeds kv_chunk_stride %lld", c, (long long)len,
+                        (long long)stride);
+        if (len > (int64_t)INT32_MAX - kBlockN) return fail(RINGATTN_EINVAL, "chunk %d too long", c);
+        ct->row_start[c] = stride > 0 ? (int64_t)c * stride : offsets[c];
+        ct->len[c] = (int32_t)len;
+        ct->tile_start[c] = (int32_t)tiles;
+        tiles += (len + kBlockN - 1) / kBlockN;
+        if (tiles > (int64_t)INT32_MAX) return fail(RINGATTN_EINVAL, "too many K/V tiles");
+    }
+    ct->tile_start[n_chunks] = (int32_t)tiles;
+    ct->n_tiles = (int32_t)tiles;
+    *kv_rows = stride > 0 ? (int64_t)n_chunks * stride : kv_len;
+    return RINGATTN_OK;
+}
+
+struct Plan {
+    int32_t n_qtiles;
+    int32_t n_splits;
+    size_t ws_bytes;
+    int64_t split_out_stride;
+    int64_t split_lse_stride;
+};
+
+// Pick the number of K/V splits.  Cost model in units of one workgroup-tile
+// (128 query rows x 64 keys): workgroups run in rounds of `slots` (two
+// resident per CU), a split of T tiles costs ceil(T / s) per workgroup, and
+// s > 1 adds the float32 partial traffic (written once, read once by the
+// merge) at HBM speed.  The constants are measured-order estimates for
+// MI355X: ~1.7 us per workgroup-tile, ~5 TB/s effective HBM.
+int choose_splits(const ringattn_shape *s, int32_t n_tiles, int32_t n_qtiles, int32_t requested) {
+    if (n_tiles <= 1) return 1;
+    const int32_t cap = n_tiles < kMaxSplits ? n_tiles : kMaxSplits;
+    if (requested > 0) return requested < cap ? requested : cap;
+    const double slots = 2.0 * cu_count_for_current_device();
+    const double base = (double)n_qtiles * s->heads * s->batch;
+    const double part_bytes = (double)s->batch * s->q_len * s->heads * (s->head_dim + 1) * 4.0;
+    const double tile_us = 1.7, bytes_per_us = 5.0e6;
+    int best = 1;
+    double best_cost = 1e300;
+    for (int sp = 1; sp <= cap; ++sp) {
+        const double rounds = std::ceil(base * sp / slots);
+        const double per_wg = std::ceil((double)n_tiles / sp);
+        double cost = rounds * per_wg * tile_us;
+        if (sp > 1) cost += (2.0 * sp * part_bytes + part_bytes) / bytes_per_us;
+        if (cost < best_cost * 0.999) {
+            best_cost = cost;
+            best = sp;
+        }
+    }
+    return best;
+}
+
+int make_plan(const ringattn_shape *s, const ChunkTable &ct, int32_t requested, Plan *p) {
+    if (requested < 0) return fail(RINGATTN_EINVAL, "requested_splits must be >= 0");
+    const int64_t n_qtiles = (s->q_len + kBlockM - 1) / kBlockM;
+    if (n_qtiles > INT32_MAX) return fail(RINGATTN_EINVAL, "q_len too large");
+    p->n_qtiles = (int32_t)n_qtiles;
+    p->n_splits = choose_splits(s, ct.n_tiles, p->n_qtiles, requested);
+    const int64_t grid = n_qtiles * s->heads * s->batch * (int64_t)p->n_splits;
+    if (grid > INT32_MAX) return fail(RINGATTN_EINVAL, "grid too large (%lld workgroups)", (long long)grid);
+    p->split_out_stride = (int64_t)s->batch * s->q_len * s->heads * s->head_dim;
+    p->split_lse_stride = (int64_t)s->batch * s->heads * s->q_len;
+    p->ws_bytes = p->n_splits > 1 ? (size_t)p->n_splits * (size_t)(p->split_out_stride + p->split_lse_stride) * 4u
+                                  : 0u;
+    // keep the lse slots 16-byte aligned after the out slots
+    if (p->n_splits > 1) p->ws_bytes += 16;
+    return RINGATTN_OK;
+}
+
+void fill_common(AttnArgs *a, const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,
+                 float scale, const ringattn_shape *s) {
+    a->q = q;
+    a->k = k;
+    a->v = v;
+    a->out = out;
+    a->lse = lse;
+    a->q_len = s->q_len;
+    a->batch = s->batch;
+    a->heads = s->heads;
+    a->scale = scale;
+    a->scale_log2e = (float)((double)scale * 1.4426950408889634);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ringattn_status_string(int status) {
+    switch (status) {
+        case RINGATTN_OK: return "RINGATTN_OK";
+        case RINGATTN_EINVAL: return "RINGATTN_EINVAL";
+        case RINGATTN_EUNSUPPORTED: return "RINGATTN_EUNSUPPORTED";
+        case RINGATTN_EWORKSPACE: return "RINGATTN_EWORKSPACE";
+        case RINGATTN_EHIP: return "RINGATTN_EHIP";
+        default: return "RINGATTN_UNKNOWN_STATUS";
+    }
+}
+
+const char *ringattn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ringattn_abi_version(void) { return kAbiVersion; }
+
+int ringattn_chunk_offsets(int64_t seq_len, int32_t n_chunks, int32_t ring_anything, int64_t *offsets_out) {
+    if (!offsets_out) return fail(RINGATTN_EINVAL, "offsets_out is NULL");
+    if (n_chunks < 1 || n_chunks > kMaxChunks)
+        return fail(RINGATTN_EINVAL, "n_chunks %d outside [1, %d]", n_chunks, kMaxChunks);
+    if (seq_len < 0) return fail(RINGATTN_EINVAL, "seq_len must be >= 0");
+    const int64_t base = seq_len / n_chunks;
+    const int64_t rem = seq_len % n_chunks;
+    if (!ring_anything && rem != 0)
+        return fail(RINGATTN_EINVAL,
+                    "seq_len %lld does not divide by ring degree %d (remainder %lld); plain ring attention needs "
+                    "an even split, Ring Anything does not",
+                    (long long)seq_len, n_chunks, (long long)rem);
+    int64_t acc = 0;
+    offsets_out[0] = 0;
+    for (int32_t c = 0; c < n_chunks; ++c) {
+        acc += base + (c < rem ? 1 : 0);
+        offsets_out[c + 1] = acc;
+    }
+    return ok();
+}
+
+int ringattn_acc_init(float *out_acc, float *lse_acc, const ringattn_shape *shape, void *stream) {
+    int st;
+    if ((st = check_shape(shape, false))) return st;
+    if ((st = check_ptr(out_acc, 16, "out_acc"))) return st;
+    if ((st = check_ptr(lse_acc, 4, "lse_acc"))) return st;
+    const int64_t n_out = (int64_t)shape->batch * shape->q_len * shape->heads * shape->head_dim;
+    const int64_t n_lse = (int64_t)shape->batch * shape->heads * shape->q_len;
+    return check_hip(launch_acc_init(out_acc, lse_acc, n_out, n_lse, (hipStream_t)stream), "acc_init launch");
+}
+
+int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk, float *out_acc,
+                  float *lse_acc, float scale, const ringattn_shape *shape, void *stream) {
+    int st;
+    if ((st = check_shape(shape, true))) return st;
+    if ((st = check_ptr(q, 16, "q"))) return st;
+    if ((st = check_ptr(out_acc, 16, "out_acc"))) return st;
+    if ((st = check_ptr(lse_acc, 4, "lse_acc"))) return st;
+    if (!std::isfinite(scale)) return fail(RINGATTN_EINVAL, "scale must be finite");
+    if (shape->kv_len == 0) return ok();  // an empty chunk is the merge identity
+    if ((st = check_ptr(k_chunk, 16, "k_chunk"))) return st;
+    if ((st = check_ptr(v_chunk, 16, "v_chunk"))) return st;
+    AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    int64_t kv_rows = 0;
+    const int64_t offs[2] = {0, shape->kv_len};
+    if ((st = build_chunk_table(offs, 1, 0, shape->kv_len, &a.ct, &kv_rows))) return st;
+    Plan p;
+    if ((st = make_plan(shape, a.ct, 1, &p))) return st;
+    fill_common(&a, q, k_chunk, v_chunk, out_acc, lse_acc, scale, shape);
+    a.kv_rows = kv_rows;
+    a.n_qtiles = p.n_qtiles;
+    a.n_splits = 1;
+    return check_hip(launch_attn(a, shape->head_dim, kModeAccum, (hipStream_t)stream), "attention launch");
+}
+
+int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
+                   const ringattn_shape *shape, void *stream) {
+    int st;
+    if ((st = check_shape(shape, false))) return st;
+    if ((st = check_ptr(out_acc, 16, "out_acc"))) return st;
+    if ((st = check_ptr(lse_acc, 4, "lse_acc"))) return st;
+    if ((st = check_ptr(out_part, 16, "out_part"))) return st;
+    if ((st = check_ptr(lse_part, 4, "lse_part"))) return st;
+    return check_hip(launch_merge2(out_acc, lse_acc, out_part, lse_part, shape->q_len, shape->batch, shape->heads,
+                                   shape->head_dim, (hipStream_t)stream),
+                     "merge launch");
+}
+
+int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offsets, int32_t n_chunks,
+                          int32_t requested_splits, int32_t *n_splits_out, size_t *workspace_bytes_out) {
+    int st;
+    if ((st = check_shape(shape, true))) return st;
+    ChunkTable ct;
+    int64_t kv_rows = 0;
+    if ((st = build_chunk_table(chunk_offsets, n_chunks, 0, shape->kv_len, &ct, &kv_rows))) return st;
+    Plan p;
+    if ((st = make_plan(shape, ct, requested_splits, &p))) return st;
+    if (n_splits_out) *n_splits_out = p.n_splits;
+    if (workspace_bytes_out) *workspace_bytes_out = p.ws_bytes;
+    return ok();
+}
+
+int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
+                     int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
+                     const ringattn_shape *shape, int32_t requested_splits, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    int st;
+    if ((st = check_shape(shape, true))) return st;
+    if ((st = check_ptr(q, 16, "q"))) return st;
+    if ((st = check_ptr(out, 16, "out"))) return st;
+    if ((st = check_ptr(lse, 4, "lse"))) return st;
+    if (!std::isfinite(scale)) return fail(RINGATTN_EINVAL, "scale must be finite");
+    AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    int64_t kv_rows = 0;
+    if ((st = build_chunk_table(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &a.ct, &kv_rows)))
+        return st;
+    Plan p;
+    if ((st = make_plan(shape, a.ct, requested_splits, &p))) return st;
+    if (a.ct.n_tiles > 0) {
+        if ((st = check_ptr(k, 16, "k"))) return st;
+        if ((st = check_ptr(v, 16, "v"))) return st;
+    }
+    if (p.n_splits > 1) {
+        if (!workspace || workspace_bytes < p.ws_bytes)
+            return fail(RINGATTN_EWORKSPACE, "plan with %d splits needs %zu workspace bytes, got %zu", p.n_splits,
+                        p.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 16)) return fail(RINGATTN_EINVAL, "workspace is not 16-byte aligned");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (a.ct.n_tiles == 0) {  // no keys at all: the empty result
+        const int64_t n_out = (int64_t)shape->batch * shape->q_len * shape->heads * shape->head_dim;
+        const int64_t n_lse = (int64_t)shape->batch * shape->heads * shape->q_len;
+        return check_hip(launch_acc_init(out, lse, n_out, n_lse, s), "acc_init launch");
+    }
+    fill_common(&a, q, k, v, out, lse, scale, shape);
+    a.kv_rows = kv_rows;
+    a.n_qtiles = p.n_qtiles;
+    a.n_splits = p.n_splits;
+    if (p.n_splits == 1) return check_hip(launch_attn(a, shape->head_dim, kModeFinal, s), "attention launch");
+
+    float *part_out = static_cast<float *>(workspace);
+    uintptr_t lse_addr = reinterpret_cast<uintptr_t>(part_out + (size_t)p.n_splits * p.split_out_stride);
+    lse_addr = (lse_addr + 15) & ~(uintptr_t)15;
+    float *part_lse = reinterpret_cast<float *>(lse_addr);
+    a.out = part_out;
+    a.lse = part_lse;
+    a.split_out_stride = p.split_out_stride;
+    a.split_lse_stride = p.split_lse_stride;
+    if ((st = check_hip(launch_attn(a, shape->head_dim, kModePartial, s), "attention launch"))) return st;
+    MergeSplitsArgs m;
+    m.part_out = part_out;
+    m.part_lse = part_lse;
+    m.out = out;
+    m.lse = lse;
+    m.q_len = shape->q_len;
+    m.batch = shape->batch;
+    m.heads = shape->heads;
+    m.n_splits = p.n_splits;
+    m.split_out_stride = p.split_out_stride;
+    m.split_lse_stride = p.split_lse_stride;
+    return check_hip(launch_merge_splits(m, shape->head_dim, s), "split merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// merge.hip -- float32 log-sum-exp merge kernels (HBM-bound, no MFMA).
+//
+// The merge of attention partials over disjoint key sets by their LSE is the
+// float32 step that ContextParallelConfig.convert_to_fp32 protects
+// (Parallelism API page, "Paralelisme").  Each thread owns 4 consecutive
+// head_dim elements of one (batch, row, head), so a wavefront reads and
+// writes 1 KiB of contiguous output per instruction.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace ringattn {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMergeThreads = 256;
+
+// out/lse <- merge over n_splits partial slots.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const MergeSplitsArgs a) {
+    constexpr int G = D / 4;
+    const int64_t gid = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    const int64_t n_rows = (int64_t)a.batch * a.q_len * a.heads;  // (b, i, h) triples
+    if (gid >= n_rows * G) return;
+    const int g = (int)(gid % G);
+    const int64_t bih = gid / G;
+    const int h = (int)(bih % a.heads);
+    const int64_t bi = bih / a.heads;
+    const int64_t i = bi % a.q_len;
+    const int64_t b = bi / a.q_len;
+    const int64_t lse_idx = (b * a.heads + h) * a.q_len + i;
+    const int64_t out_idx = bih * D + 4 * g;
+
+    float mx = -INFINITY;
+    for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, a.part_lse[s * a.split_lse_stride + lse_idx]);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lse = -INFINITY;
+    if (mx != -INFINITY) {
+        float sum = 0.f;
+        for (int s = 0; s < a.n_splits; ++s) {
+            const float l = a.part_lse[s * a.split_lse_stride + lse_idx];
+            if (l != -INFINITY) sum += expf(l - mx);
+        }
+        lse = mx + logf(sum);
+        for (int s = 0; s < a.n_splits; ++s) {
+            const float l = a.part_lse[s * a.split_lse_stride + lse_idx];
+            if (l == -INFINITY) continue;  // empty split: never multiplied
+            acc += expf(l - lse) * *(const f32x4 *)(a.part_out + s * a.split_out_stride + out_idx);
+        }
+    }
+    *(f32x4 *)(a.out + out_idx) = acc;
+    if (g == 0) a.lse[lse_idx] = lse;
+}
+
+// acc <- merge(acc, part) in place.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge2_kernel(float *out_acc, float *lse_acc, const float *out_part,
+                                                              const float *lse_part, int64_t q_len, int32_t batch,
+                                                              int32_t heads) {
+    constexpr int G = D / 4;
+    const int64_t gid = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    const int64_t n_rows = (int64_t)batch * q_len * heads;
+    if (gid >= n_rows * G) return;
+    const int g = (int)(gid % G);
+    const int64_t bih = gid / G;
+    const int h = (int)(bih % heads);
+    const int64_t bi = bih / heads;
+    const int64_t i = bi % q_len;
+    const int64_t b = bi / q_len;
+    const int64_t lse_idx = (b * heads + h) * q_len + i;
+    const int64_t out_idx = bih * D + 4 * g;
+
+    const float la = lse_acc[lse_idx];
+    const float lb = lse_part[lse_idx];
+    f32x4 *pa = (f32x4 *)(out_acc + out_idx);
+    const f32x4 *pb = (const f32x4 *)(out_part + out_idx);
+    f32x4 res;
+    float lse;
+    if (la == -INFINITY && lb == -INFINITY) {
+        res = f32x4{0.f, 0.f, 0.f, 0.f};
+        lse = -INFINITY;
+    } else if (la == -INFINITY) {
+        res = *pb;
+        lse = lb;
+    } else if (lb == -INFINITY) {
+        res = *pa;
+        lse = la;
+    } else {
+        lse = fmaxf(la, lb) + log1pf(expf(-fabsf(la - lb)));
+        res = expf(la - lse) * (*pa) + expf(lb - lse) * (*pb);
+    }
+    *pa = res;
+    // The D/4 threads of a row are consecutive lanes of one wavefront, so all
+    // of them have read lse_acc (above) before lane g == 0 overwrites it.
+    if (g == 0) lse_acc[lse_idx] = lse;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void acc_init_kernel(float *out, float *lse, int64_t n_out4,
+                                                                int64_t n_lse) {
+    const int64_t gid = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    if (gid < n_out4) ((f32x4 *)out)[gid] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (gid < n_lse) lse[gid] = -INFINITY;
+}
+
+inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kMergeThreads - 1) / kMergeThreads); }
+
+}  // namespace
+
+hipError_t launch_merge_splits(const MergeSplitsArgs &a, int head_dim, hipStream_t stream) {
+    const int64_t n = (int64_t)a.batch * a.q_len * a.heads * (head_dim / 4);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(merge_splits_kernel<128>, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(merge_splits_kernel<64>, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge2(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
+                         int64_t q_len, int32_t batch, int32_t heads, int32_t head_dim, hipStream_t stream) {
+    const int64_t n = (int64_t)batch * q_len * heads * (head_dim / 4);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(merge2_kernel<128>, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, out_acc, lse_acc,
+                           out_part, lse_part, q_len, batch, heads);
+    else
+        hipLaunchKernelGGL(merge2_kernel<64>, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, out_acc, lse_acc,
+                           out_part, lse_part, q_len, batch, heads);
+    return hipGetLastError();
+}
+
+hipError_t launch_acc_init(float *out, float *lse, int64_t n_out, int64_t n_lse, hipStream_t stream) {
+    const int64_t n4 = n_out / 4;
+    const int64_t n = n4 > n_lse ? n4 : n_lse;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(acc_init_kernel, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, out, lse, n4, n_lse);
+    return hipGetLastError();
+}
+
+}  // namespace ringattn

@@ -1,0 +1,251 @@
+"""Python surface of the ring-shard attention library (torch tensors in, out).
+
+PyTorch only provides device memory and the stream; every computation runs in
+the HIP library through the C ABI (``include/ringattn.h``).  Tensors are BSHD
+(``[batch, seq, heads, head_dim]``, contiguous): Q/K/V bf16 on a ROCm device,
+outputs float32; LSE is ``[batch, heads, q_len]`` float32 (natural log).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import RingAttnError, Shape, check, lib, offsets_array
+
+
+# ------------------------------------------------------------------ config --
+
+@dataclasses.dataclass(frozen=True)
+class RingConfig:
+    """The subset of ``ContextParallelConfig`` (Parallelism API page) that maps
+    onto one GPU's share of ring attention, with the pages' rules checked:
+
+    * ``ring_degree``: number of K/V chunks (ring ranks), >= 1;
+    * ``ulysses_degree``: head groups; with ring_degree = 1 this GPU's share is
+      full-sequence attention over heads / ulysses_degree heads;
+    * ``convert_to_fp32``: output and LSE merged in float32 (default True, the
+      only mode built);
+    * ``rotate_method``: only ``"allgather"`` is supported (as on the page);
+    * ``ring_anything``: uneven chunks; needs ring_degree > 1 and
+      ulysses_degree == 1, inference only, no attention mask (guide, variant
+      table and section "Ring Anything Attention").
+    """
+
+    ring_degree: int = 1
+    ulysses_degree: int = 1
+    convert_to_fp32: bool = True
+    rotate_method: str = "allgather"
+    ring_anything: bool = False
+
+    def __post_init__(self):
+        if self.ring_degree < 1 or self.ulysses_degree < 1:
+            raise ValueError("ring_degree and ulysses_degree must be >= 1")
+        if not self.convert_to_fp32:
+            raise ValueError("convert_to_fp32=False is not built; the merge is always float32")
+        if self.rotate_method != "allgather":
+            raise ValueError(f"rotate_method {self.rotate_method!r} is not supported; only 'allgather'")
+        if self.ring_anything and (self.ring_degree <= 1 or self.ulysses_degree != 1):
+            raise ValueError("ring_anything needs ring_degree > 1 and ulysses_degree == 1")
+        if self.ring_degree > _lib.RINGATTN_MAX_CHUNKS:
+            raise ValueError(f"ring_degree above {_lib.RINGATTN_MAX_CHUNKS} is not supported")
+
+
+# ------------------------------------------------------------- marshalling --
+
+def _stream_handle(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_bf16(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [batch, seq, heads, head_dim] (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous BSHD")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device (got {t.device})")
+
+
+def _check_f32(t: torch.Tensor, name: str, shape: Tuple[int, ...], device: torch.device) -> None:
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} "
+                         f"(got {t.dtype} {tuple(t.shape)})")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+
+
+def _shape(q: torch.Tensor, kv_len: int) -> Shape:
+    B, Sq, H, D = q.shape
+    return Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=kv_len)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(head_dim) as a float32 value."""
+    return float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32).item())
+
+
+# ------------------------------------------------------------------- calls --
+
+def chunk_offsets(seq_len: int, n_chunks: int, ring_anything: bool = False) -> List[int]:
+    """Chunk partition computed by the library (host code)."""
+    arr = (ctypes.c_int64 * (n_chunks + 1))() if n_chunks >= 0 else None
+    if arr is None:
+        raise ValueError("n_chunks must be >= 0")
+    check(lib().ringattn_chunk_offsets(int(seq_len), int(n_chunks), int(bool(ring_anything)), arr),
+          "ringattn_chunk_offsets")
+    return list(arr)
+
+
+_library_chunk_offsets = chunk_offsets
+
+
+def acc_init(out_acc: torch.Tensor, lse_acc: torch.Tensor, stream=None) -> None:
+    """Set accumulators to the empty state (out = 0, lse = -inf)."""
+    B, Sq, H, D = out_acc.shape
+    _check_f32(lse_acc, "lse_acc", (B, H, Sq), out_acc.device)
+    shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=0)
+    check(lib().ringattn_acc_init(_ptr(out_acc), _ptr(lse_acc), ctypes.byref(shape),
+                                  _stream_handle(out_acc.device, stream)), "ringattn_acc_init")
+
+
+def new_accumulators(q: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Allocate float32 accumulators for q and set them to the empty state."""
+    B, Sq, H, D = q.shape
+    out = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    acc_init(out, lse, stream)
+    return out, lse
+
+
+def step(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out_acc: torch.Tensor,
+         lse_acc: torch.Tensor, scale: Optional[float] = None, stream=None) -> None:
+    """One ring step: attend q to one K/V chunk and LSE-merge into the float32
+    accumulators in place (the merge is fused into the kernel epilogue)."""
+    _check_bf16(q, "q")
+    _check_bf16(k_chunk, "k_chunk")
+    _check_bf16(v_chunk, "v_chunk")
+    B, Sq, H, D = q.shape
+    if k_chunk.shape != v_chunk.shape or k_chunk.shape[0] != B or k_chunk.shape[2:] != q.shape[2:]:
+        raise ValueError(f"k/v chunk shapes {tuple(k_chunk.shape)} / {tuple(v_chunk.shape)} do not match q")
+    _check_f32(out_acc, "out_acc", (B, Sq, H, D), q.device)
+    _check_f32(lse_acc, "lse_acc", (B, H, Sq), q.device)
+    if scale is None:
+        scale = default_scale(D)
+    shape = _shape(q, k_chunk.shape[1])
+    check(lib().ringattn_step(_ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(out_acc), _ptr(lse_acc),
+                              ctypes.c_float(scale), ctypes.byref(shape), _stream_handle(q.device, stream)),
+          "ringattn_step")
+
+
+def merge(out_acc: torch.Tensor, lse_acc: torch.Tensor, out_part: torch.Tensor, lse_part: torch.Tensor,
+          stream=None) -> None:
+    """LSE-merge a float32 partial into the accumulators in place."""
+    B, Sq, H, D = out_acc.shape
+    _check_f32(out_acc, "out_acc", (B, Sq, H, D), out_acc.device)
+    _check_f32(out_part, "out_part", (B, Sq, H, D), out_acc.device)
+    _check_f32(lse_acc, "lse_acc", (B, H, Sq), out_acc.device)
+    _check_f32(lse_part, "lse_part", (B, H, Sq), out_acc.device)
+    shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=0)
+    check(lib().ringattn_merge(_ptr(out_acc), _ptr(lse_acc), _ptr(out_part), _ptr(lse_part),
+                               ctypes.byref(shape), _stream_handle(out_acc.device, stream)), "ringattn_merge")
+
+
+def forward_plan(q_shape: Sequence[int], offsets: Sequence[int], requested_splits: int = 0) -> Tuple[int, int]:
+    """(n_splits, workspace_bytes) the library will use for a forward call."""
+    B, Sq, H, D = q_shape
+    shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=int(offsets[-1]))
+    n = ctypes.c_int32(0)
+    ws = ctypes.c_size_t(0)
+    arr = offsets_array(offsets)
+    check(lib().ringattn_forward_plan(ctypes.byref(shape), arr, len(offsets) - 1, int(requested_splits),
+                                      ctypes.byref(n), ctypes.byref(ws)), "ringattn_forward_plan")
+    return n.value, ws.value
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+            chunk_offsets: Optional[Sequence[int]] = None,
+            ring_degree: Optional[int] = None,
+            ring_anything: bool = False,
+            kv_chunk_stride: int = 0,
+            scale: Optional[float] = None,
+            n_splits: int = 0,
+            out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None,
+            convert_to_fp32: bool = True,
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The whole shard: q attends to every K/V chunk; returns (out fp32, lse fp32).
+
+    Give either ``chunk_offsets`` (n_chunks + 1 host integers) or
+    ``ring_degree`` (+ ``ring_anything``) to partition the K/V rows.  With
+    ``kv_chunk_stride`` > 0, k/v are the padded all-gather buffer of Ring
+    Anything (chunk c at rows ``c * kv_chunk_stride``, true lengths from the
+    offsets).  Buffers not passed in are allocated with torch on q's device.
+    """
+    if not convert_to_fp32:
+        raise ValueError("convert_to_fp32=False is not built; the merge is always float32")
+    _check_bf16(q, "q")
+    _check_bf16(k, "k")
+    _check_bf16(v, "v")
+    B, Sq, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError(f"k/v shapes {tuple(k.shape)} / {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if chunk_offsets is None:
+        if ring_degree is None:
+            ring_degree = 1
+        n = int(ring_degree)
+        if kv_chunk_stride:
+            raise ValueError("kv_chunk_stride needs explicit chunk_offsets")
+        chunk_offsets = _library_chunk_offsets(k.shape[1], n, ring_anything)
+    offs = [int(x) for x in chunk_offsets]
+    n_chunks = len(offs) - 1
+    rows_needed = n_chunks * int(kv_chunk_stride) if kv_chunk_stride else offs[-1]
+    if k.shape[1] != rows_needed:
+        raise ValueError(f"k/v hold {k.shape[1]} rows per batch, the chunk layout needs {rows_needed}")
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _check_f32(out, "out", (B, Sq, H, D), q.device)
+    _check_f32(lse, "lse", (B, H, Sq), q.device)
+    shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=offs[-1])
+    arr = offsets_array(offs)
+    if workspace is None:
+        nsp = ctypes.c_int32(0)
+        ws_bytes = ctypes.c_size_t(0)
+        check(lib().ringattn_forward_plan(ctypes.byref(shape), arr, n_chunks, int(n_splits), ctypes.byref(nsp),
+                                          ctypes.byref(ws_bytes)), "ringattn_forward_plan")
+        if ws_bytes.value:
+            workspace = torch.empty((ws_bytes.value,), dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib().ringattn_forward(_ptr(q), _ptr(k), _ptr(v), arr, n_chunks, int(kv_chunk_stride), _ptr(out), _ptr(lse),
+                                 ctypes.c_float(scale), ctypes.byref(shape), int(n_splits), ws_ptr, ws_len,
+                                 _stream_handle(q.device, stream)), "ringattn_forward")
+    return out, lse
+
+
+def ring_shard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, config: RingConfig, *,
+               scale: Optional[float] = None, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward for one GPU's share under a ``RingConfig``: ring_degree chunks
+    of the K/V sequence (Ring Anything if set).  For the Ulysses share pass
+    the head subset as q/k/v and ring_degree = 1."""
+    return forward(q, k, v, ring_degree=config.ring_degree, ring_anything=config.ring_anything,
+                   scale=scale, convert_to_fp32=config.convert_to_fp32, **kw)

@@ -1,0 +1,171 @@
+/*
+ * ringattn.h -- C ABI of the MI355X (gfx950) ring-attention shard library.
+ *
+ * One GPU's share of ring attention: a local query shard Q attends to N
+ * key/value sequence chunks, one non-causal softmax-attention pass per chunk,
+ * and the chunk partials (output, log-sum-exp) are merged in float32.
+ * Sources of the semantics:
+ *   - Context-parallelism guide ("Paralelisme konteks", diffusers v0.43.0),
+ *     section "Ring Attention": each GPU attends its queries to the K/V block
+ *     it holds, passes the block on, and after one full turn has seen the K/V
+ *     of every token.
+ *   - Parallelism API page ("Paralelisme"), ContextParallelConfig:
+ *     ring_degree (N chunks, N iterations), convert_to_fp32 (output and LSE
+ *     kept in float32 for the merge; default True, the only mode built here),
+ *     rotate_method "allgather" (every chunk is resident before the loop),
+ *     ring_anything (any sequence length; uneven chunks).
+ *   - Same guide, section "Ring Anything Attention": local K/V padded to the
+ *     longest local length, all-gathered, and cut back to each block's true
+ *     length before attention; inference only, no attention mask.
+ *   - Same guide, section "Perhatian Ulysses": after the all-to-all each GPU
+ *     holds every token for a subset of heads; its share is full-sequence
+ *     attention over those heads (ringattn_forward with one chunk).
+ *
+ * Conventions for every call:
+ *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *   - Q, K, V and outputs are BSHD: [batch, seq, heads, head_dim], contiguous,
+ *     head_dim innermost.  LSE is [batch, heads, q_len], float32, natural log,
+ *     with the softmax scale inside: lse = ln sum_j exp(scale * q . k_j).
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never frees or keeps them.  Q/K/V/out/workspace must be 16-byte aligned,
+ *     LSE 4-byte aligned.  Chunk offsets are HOST memory, read during the call.
+ *   - No call allocates device memory or synchronises.  All GPU work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *     runs asynchronously.  Calls that write the same buffers on one stream
+ *     are ordered; on different streams the caller orders them.
+ *   - Every argument is validated before any GPU work is enqueued; on an
+ *     error status nothing is launched and no buffer is written.
+ *   - head_dim must be 64 or 128 (RINGATTN_EUNSUPPORTED otherwise).
+ *   - Status codes are below; ringattn_last_error() gives the message of the
+ *     last failing call on the calling thread.
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RINGATTN_MAX_CHUNKS 128 /* largest ring degree one forward call accepts */
+
+typedef struct ringattn_shape {
+    int32_t batch;    /* B >= 1 */
+    int32_t heads;    /* H >= 1 heads held by this GPU */
+    int32_t head_dim; /* D: 64 or 128 */
+    int32_t reserved; /* must be 0 */
+    int64_t q_len;    /* Sq >= 1 local query rows */
+    int64_t kv_len;   /* key/value rows: this chunk's (step) or all chunks' (forward) */
+} ringattn_shape;
+
+enum ringattn_status {
+    RINGATTN_OK = 0,
+    RINGATTN_EINVAL = -1,        /* bad argument: null/misaligned pointer, bad size or offsets */
+    RINGATTN_EUNSUPPORTED = -2,  /* valid but not built: head_dim other than 64/128 */
+    RINGATTN_EWORKSPACE = -3,    /* workspace missing or smaller than the plan needs */
+    RINGATTN_EHIP = -4           /* the HIP runtime reported an error (message has it) */
+};
+
+/* Name of a status code ("RINGATTN_OK", ...); never NULL. */
+const char *ringattn_status_string(int status);
+
+/* Message describing the last failing call on this thread ("" if none).
+ * The pointer stays valid until the next library call on this thread. */
+const char *ringattn_last_error(void);
+
+/* Library ABI version (incremented on any signature change). */
+int32_t ringattn_abi_version(void);
+
+/*
+ * Chunk partition of a length-seq_len sequence over n_chunks ring ranks.
+ * Writes offsets_out[0..n_chunks] (host memory, n_chunks + 1 entries):
+ * offsets_out[0] = 0, offsets_out[n_chunks] = seq_len, chunk i is tokens
+ * [offsets_out[i], offsets_out[i+1]).
+ *   ring_anything = 0: plain ring attention; seq_len must divide evenly by
+ *     n_chunks (guide, variant table), else RINGATTN_EINVAL.
+ *   ring_anything != 0: any seq_len >= 0; the first (seq_len mod n_chunks)
+ *     chunks hold one extra token, so every chunk fits the padded length
+ *     ceil(seq_len / n_chunks) that Ring Anything pads to.
+ * n_chunks must be in [1, RINGATTN_MAX_CHUNKS].  Pure host code.
+ */
+int ringattn_chunk_offsets(int64_t seq_len, int32_t n_chunks, int32_t ring_anything,
+                           int64_t *offsets_out);
+
+/*
+ * Set a float32 accumulator to the empty merge state: out_acc = 0 and
+ * lse_acc = -inf (the identity of the LSE merge).  out_acc is
+ * [B, q_len, H, D], lse_acc is [B, H, q_len].  shape->kv_len is ignored.
+ */
+int ringattn_acc_init(float *out_acc, float *lse_acc, const ringattn_shape *shape, void *stream);
+
+/*
+ * One ring step: attend q ([B, q_len, H, D] bf16) to one K/V chunk
+ * (k_chunk, v_chunk: [B, kv_len, H, D] bf16; kv_len = shape->kv_len) with
+ * softmax scale `scale`, and merge the chunk partial (its normalised output
+ * and LSE) into the float32 accumulators out_acc / lse_acc in place:
+ *     lse' = max(a, b) + ln(1 + exp(-|a - b|))
+ *     out' = exp(a - lse') * out_acc + exp(b - lse') * out_chunk
+ * with a = lse_acc, b = the chunk's LSE; where a = -inf the chunk partial is
+ * copied (the old accumulator output is never multiplied).  The merge is
+ * fused into the attention kernel's epilogue.  kv_len = 0 is a no-op.
+ * Start from ringattn_acc_init; after all N chunks the accumulators hold the
+ * shard's attention output and LSE.  scale must be finite.
+ */
+int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk,
+                  float *out_acc, float *lse_acc, float scale,
+                  const ringattn_shape *shape, void *stream);
+
+/*
+ * Merge a partial (out_part [B, q_len, H, D], lse_part [B, H, q_len], float32)
+ * into the accumulators in place, with the same formula as ringattn_step.
+ * A partial with lse = -inf is the identity; if both are -inf the result is
+ * out = 0, lse = -inf.  shape->kv_len is ignored.
+ */
+int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
+                   const ringattn_shape *shape, void *stream);
+
+/*
+ * Launch plan of ringattn_forward for these arguments: the number of
+ * key/value splits it will use (independent partial passes over disjoint
+ * ranges of K/V tiles, merged at the end by their LSE) and the workspace
+ * bytes that plan needs (0 when n_splits is 1).
+ *   requested_splits = 0: the library picks from the shape and the GPU's
+ *     compute-unit count; > 0: use that many (clamped to the K/V tile count).
+ * n_splits_out and workspace_bytes_out may each be NULL.
+ */
+int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offsets, int32_t n_chunks,
+                          int32_t requested_splits, int32_t *n_splits_out, size_t *workspace_bytes_out);
+
+/*
+ * The whole shard in one call: q attends to all n_chunks K/V chunks and the
+ * float32 result is written to out ([B, q_len, H, D]) and lse ([B, H, q_len]).
+ * chunk_offsets (host, n_chunks + 1 entries) must start at 0, not decrease
+ * and end at shape->kv_len; chunk c is rows [offsets[c], offsets[c+1]).
+ * Where those rows live in k / v ([B, rows, H, D] bf16):
+ *   kv_chunk_stride = 0: packed -- chunk c is rows offsets[c].. of k and v,
+ *     which hold shape->kv_len rows per batch;
+ *   kv_chunk_stride > 0: the padded all-gather buffer of Ring Anything --
+ *     chunk c starts at row c * kv_chunk_stride and holds its true length
+ *     offsets[c+1] - offsets[c] <= kv_chunk_stride; k and v hold
+ *     n_chunks * kv_chunk_stride rows per batch and the padding rows are
+ *     never read.
+ * Chunks are visited in order 0..n_chunks-1 with an online softmax whose
+ * running float32 (max, sum, output) state is the LSE merge of the chunk
+ * partials so far.  requested_splits as in ringattn_forward_plan; when the
+ * plan has more than one split, workspace must hold the planned bytes
+ * (RINGATTN_EWORKSPACE otherwise).  workspace may be NULL with
+ * workspace_bytes = 0 only when the plan needs none.  With kv_len = 0 the
+ * result is out = 0, lse = -inf.
+ */
+int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const int64_t *chunk_offsets, int32_t n_chunks, int64_t kv_chunk_stride,
+                     float *out, float *lse, float scale, const ringattn_shape *shape,
+                     int32_t requested_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_H */

@@ -1,0 +1,216 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, its chunk partition matches the oracle bit for bit, and every
+validation error is reported before any GPU work (no device needed)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from context_attention_diffusion_ringattn_amd import _lib
+from context_attention_diffusion_ringattn_amd._lib import Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ringattn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ringattn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_header_symbols_exported(L):
+    names = header_functions()
+    assert names, "no declarations found in the header"
+    assert sorted(_lib.EXPORTED_SYMBOLS) == names
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    dyn = set(re.findall(r"\bT (ringattn_[a-z0-9_]+)", out))
+    assert set(names) <= dyn
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.ringattn_abi_version() == 1
+    assert _lib.status_string(0) == "RINGATTN_OK"
+    assert _lib.status_string(-1) == "RINGATTN_EINVAL"
+    assert _lib.status_string(-2) == "RINGATTN_EUNSUPPORTED"
+    assert _lib.status_string(-3) == "RINGATTN_EWORKSPACE"
+    assert _lib.status_string(-4) == "RINGATTN_EHIP"
+    assert _lib.status_string(7) == "RINGATTN_UNKNOWN_STATUS"
+
+
+def _lib_offsets(L, S, N, ra):
+    arr = (ctypes.c_int64 * (N + 1))()
+    st = L.ringattn_chunk_offsets(S, N, ra, arr)
+    return st, list(arr)
+
+
+def test_offsets_bit_exact_vs_oracle(L):
+    for S in range(0, 301):
+        for N in range(1, 17):
+            st, offs = _lib_offsets(L, S, N, 1)
+            assert st == 0 and offs == oracle.chunk_offsets(S, N, ring_anything=True), (S, N)
+            st, offs = _lib_offsets(L, S, N, 0)
+            if S % N == 0:
+                assert st == 0 and offs == oracle.chunk_offsets(S, N), (S, N)
+            else:
+                assert st == _lib.RINGATTN_EINVAL
+                assert "divide" in _lib.last_error()
+
+
+def test_offsets_workloads_and_limits(L):
+    for S, N, ra in ((256, 2, 0), (4608, 4, 0), (4611, 8, 1), (16384, 1, 0), (65536, 8, 0), (4481, 4, 1),
+                     (10**12 + 7, 128, 1)):
+        st, offs = _lib_offsets(L, S, N, ra)
+        assert st == 0 and offs == oracle.chunk_offsets(S, N, ring_anything=bool(ra))
+    assert _lib_offsets(L, 10, 0, 1)[0] == _lib.RINGATTN_EINVAL
+    assert _lib_offsets(L, 10, 129, 1)[0] == _lib.RINGATTN_EINVAL
+    assert _lib_offsets(L, -1, 2, 1)[0] == _lib.RINGATTN_EINVAL
+    assert L.ringattn_chunk_offsets(10, 2, 0, None) == _lib.RINGATTN_EINVAL
+
+
+# Fake but aligned device addresses: every call below must fail validation
+# before it could touch them.
+P = ctypes.c_void_p(1 << 20)
+P_MISALIGNED = ctypes.c_void_p((1 << 20) + 8)
+
+
+def shape(B=1, H=2, D=64, Sq=128, Skv=256, reserved=0):
+    return Shape(batch=B, heads=H, head_dim=D, reserved=reserved, q_len=Sq, kv_len=Skv)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(B=0), _lib.RINGATTN_EINVAL),
+    (dict(H=0), _lib.RINGATTN_EINVAL),
+    (dict(Sq=0), _lib.RINGATTN_EINVAL),
+    (dict(Skv=-1), _lib.RINGATTN_EINVAL),
+    (dict(reserved=1), _lib.RINGATTN_EINVAL),
+    (dict(D=96), _lib.RINGATTN_EUNSUPPORTED),
+    (dict(D=256), _lib.RINGATTN_EUNSUPPORTED),
+])
+def test_step_shape_errors(L, bad, code):
+    s = shape(**bad)
+    st = L.ringattn_step(P, P, P, P, P, ctypes.c_float(0.125), ctypes.byref(s), None)
+    assert st == code
+    assert _lib.last_error()
+
+
+def test_step_pointer_errors(L):
+    s = shape()
+    f = ctypes.c_float(0.125)
+    assert L.ringattn_step(None, P, P, P, P, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_step(P, None, P, P, P, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_step(P, P, None, P, P, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_step(P, P, P, None, P, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_step(P, P, P, P, None, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_step(P_MISALIGNED, P, P, P, P, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert "aligned" in _lib.last_error()
+    assert L.ringattn_step(P, P, P, P, P, ctypes.c_float(float("inf")), ctypes.byref(s), None) == \
+        _lib.RINGATTN_EINVAL
+    assert L.ringattn_step(P, P, P, P, P, f, None, None) == _lib.RINGATTN_EINVAL
+
+
+def test_step_empty_chunk_is_noop(L):
+    """kv_len = 0: nothing to attend to; the call succeeds without touching
+    any buffer (null K/V are accepted)."""
+    s = shape(Skv=0)
+    assert L.ringattn_step(P, None, None, P, P, ctypes.c_float(0.125), ctypes.byref(s), None) == 0
+
+
+def _fwd(L, offs, s, stride=0, splits=0, ws=None, ws_bytes=0, q=P, k=P, v=P, out=P, lse=P, scale=0.125):
+    arr = _lib.offsets_array(offs) if offs is not None else None
+    return L.ringattn_forward(q, k, v, arr, (len(offs) - 1) if offs is not None else 1, stride, out, lse,
+                              ctypes.c_float(scale), ctypes.byref(s), splits, ws, ws_bytes, None)
+
+
+def test_forward_offset_errors(L):
+    s = shape(Skv=256)
+    assert _fwd(L, None, s) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [1, 128, 256], s) == _lib.RINGATTN_EINVAL            # does not start at 0
+    assert _fwd(L, [0, 128, 255], s) == _lib.RINGATTN_EINVAL            # does not end at kv_len
+    assert _fwd(L, [0, 200, 100, 256], s) == _lib.RINGATTN_EINVAL       # decreasing
+    assert _fwd(L, [0] + [2] * 129 + [256], s) == _lib.RINGATTN_EINVAL  # too many chunks
+    assert _fwd(L, [0, 128, 256], s, stride=100) == _lib.RINGATTN_EINVAL  # chunk longer than the stride
+    assert _fwd(L, [0, 128, 256], s, stride=-1) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], s, splits=-1) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], s, out=P_MISALIGNED) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], s, q=None) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], s, scale=float("nan")) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], shape(D=80)) == _lib.RINGATTN_EUNSUPPORTED
+
+
+def test_forward_workspace_error(L):
+    """A plan with several splits and no (or too small a) workspace is refused."""
+    s = shape(B=1, H=2, D=128, Sq=128, Skv=4096)
+    n = ctypes.c_int32()
+    ws = ctypes.c_size_t()
+    offs = _lib.offsets_array([0, 4096])
+    assert L.ringattn_forward_plan(ctypes.byref(s), offs, 1, 4, ctypes.byref(n), ctypes.byref(ws)) == 0
+    assert n.value == 4 and ws.value >= 4 * (128 * 2 * 128 + 2 * 128) * 4
+    assert _fwd(L, [0, 4096], s, splits=4) == _lib.RINGATTN_EWORKSPACE
+    assert _fwd(L, [0, 4096], s, splits=4, ws=P, ws_bytes=ws.value - 1) == _lib.RINGATTN_EWORKSPACE
+    assert _fwd(L, [0, 4096], s, splits=4, ws=P_MISALIGNED, ws_bytes=ws.value) == _lib.RINGATTN_EINVAL
+
+
+def test_forward_plan_properties(L):
+    """Plans: a single split needs no workspace; splits never exceed the number
+    of K/V tiles; the plan is deterministic."""
+    for (B, H, D, Sq, offs) in ((1, 24, 128, 8192, oracle.chunk_offsets(65536, 8)),
+                                (1, 24, 128, 1152, oracle.chunk_offsets(4608, 4)),
+                                (1, 24, 128, 577, oracle.chunk_offsets(4611, 8, True)),
+                                (1, 6, 128, 16384, [0, 16384]),
+                                (1, 2, 64, 128, [0, 128, 256]),
+                                (1, 1, 64, 1, [0, 1])):
+        s = shape(B=B, H=H, D=D, Sq=Sq, Skv=offs[-1])
+        arr = _lib.offsets_array(offs)
+        n = ctypes.c_int32()
+        ws = ctypes.c_size_t()
+        assert L.ringattn_forward_plan(ctypes.byref(s), arr, len(offs) - 1, 0, ctypes.byref(n), ctypes.byref(ws)) == 0
+        tiles = sum(-(-(b - a) // 64) for a, b in zip(offs, offs[1:]))
+        assert 1 <= n.value <= max(1, tiles)
+        assert (ws.value == 0) == (n.value == 1)
+        n2 = ctypes.c_int32()
+        L.ringattn_forward_plan(ctypes.byref(s), arr, len(offs) - 1, 0, ctypes.byref(n2), None)
+        assert n2.value == n.value
+
+
+def test_merge_and_init_errors(L):
+    s = shape()
+    assert L.ringattn_merge(None, P, P, P, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_merge(P, P, P_MISALIGNED, P, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_merge(P, P, P, P, ctypes.byref(shape(D=32)), None) == _lib.RINGATTN_EUNSUPPORTED
+    assert L.ringattn_acc_init(P, None, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_acc_init(P, P, ctypes.byref(shape(Sq=0)), None) == _lib.RINGATTN_EINVAL
+
+
+def test_python_config_rules():
+    from context_attention_diffusion_ringattn_amd import RingConfig
+    RingConfig(ring_degree=8)
+    RingConfig(ring_degree=8, ring_anything=True)
+    with pytest.raises(ValueError):
+        RingConfig(ring_degree=1, ring_anything=True)
+    with pytest.raises(ValueError):
+        RingConfig(ring_degree=2, ulysses_degree=2, ring_anything=True)
+    with pytest.raises(ValueError):
+        RingConfig(ring_degree=2, convert_to_fp32=False)
+    with pytest.raises(ValueError):
+        RingConfig(ring_degree=2, rotate_method="alltoall")
+    with pytest.raises(ValueError):
+        RingConfig(ring_degree=0)
+
+
+def test_python_offsets_wrapper():
+    from context_attention_diffusion_ringattn_amd import RingAttnError, chunk_offsets
+    assert chunk_offsets(4611, 8, ring_anything=True) == oracle.chunk_offsets(4611, 8, ring_anything=True)
+    with pytest.raises(RingAttnError):
+        chunk_offsets(4481, 4)

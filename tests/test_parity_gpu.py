@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same bf16 inputs.
+
+Tolerances (written here, used everywhere below): max |out - oracle| <= 1e-2
+and max |lse - oracle| <= 1e-3, elementwise over every compared value.  Small
+workloads are compared in full; the full-size Ulysses and video shards are run
+in the launch configuration the benchmark times and compared on sampled rows
+(every head) that the oracle computes one by one.
+"""
+
+import functools
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from context_attention_diffusion_ringattn_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def ra():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    import context_attention_diffusion_ringattn_amd as ra_mod
+    ra_mod._lib.lib()  # fail loudly if the library is missing
+    return ra_mod
+
+
+def dev(t):
+    return t.to("cuda:0")
+
+
+def errors(gpu_out, gpu_lse, ref_out, ref_lse):
+    o = gpu_out.detach().to("cpu", torch.float64).numpy()
+    l = gpu_lse.detach().to("cpu", torch.float64).numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), "non-finite GPU result"
+    return float(np.max(np.abs(o - ref_out))), float(np.max(np.abs(l - ref_lse)))
+
+
+def assert_close(gpu_out, gpu_lse, ref_out, ref_lse, what):
+    eo, el = errors(gpu_out, gpu_lse, ref_out, ref_lse)
+    print(f"{what}: max|dout|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= OUT_TOL, f"{what}: out error {eo}"
+    assert el <= LSE_TOL, f"{what}: lse error {el}"
+
+
+@functools.lru_cache(maxsize=None)
+def workload_inputs(name):
+    return W.make_inputs(name)
+
+
+@functools.lru_cache(maxsize=None)
+def workload_oracle(name):
+    x = workload_inputs(name)
+    return oracle.attention_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]), x["scale"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux", "ring_anything"])
+def test_forward_small_workloads(ra, name):
+    """Tiny, Flux-like and Ring Anything shards, compared in full, with the
+    library's own partition and launch plan."""
+    x = workload_inputs(name)
+    w = x["workload"]
+    print(f"case {name}: q{tuple(x['q'].shape)} kv{tuple(x['k'].shape)}", flush=True)
+    offs = ra.chunk_offsets(w.seq_len, w.n_chunks, w.ring_anything)
+    assert offs == oracle.chunk_offsets(w.seq_len, w.n_chunks, w.ring_anything)
+    assert offs[1] == w.q_rows
+    out, lse = ra.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]), chunk_offsets=offs, scale=x["scale"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = workload_oracle(name)
+    assert_close(out, lse, ref_out, ref_lse, f"forward {name}")
+
+
+@pytest.mark.parametrize("name", ["flux", "ring_anything"])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_forward_forced_splits(ra, name, splits):
+    """Every split count gives the oracle's result (the split partials are
+    merged by LSE in the merge kernel)."""
+    x = workload_inputs(name)
+    w = x["workload"]
+    print(f"case {name} splits={splits}", flush=True)
+    out, lse = ra.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]), ring_degree=w.n_chunks,
+                          ring_anything=w.ring_anything, scale=x["scale"], n_splits=splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = workload_oracle(name)
+    assert_close(out, lse, ref_out, ref_lse, f"forward {name} splits={splits}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux", "ring_anything"])
+def test_step_path_matches_oracle_and_forward(ra, name):
+    """The ring's own loop: accumulators initialised to (0, -inf), then one
+    ringattn_step per chunk with the merge fused in the epilogue."""
+    x = workload_inputs(name)
+    w = x["workload"]
+    print(f"case step {name}", flush=True)
+    offs = oracle.chunk_offsets(w.seq_len, w.n_chunks, w.ring_anything)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    out_acc, lse_acc = ra.new_accumulators(q)
+    for c in range(w.n_chunks):
+        ra.step(q, k[:, offs[c]:offs[c + 1]].contiguous(), v[:, offs[c]:offs[c + 1]].contiguous(),
+                out_acc, lse_acc, scale=x["scale"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = workload_oracle(name)
+    assert_close(out_acc, lse_acc, ref_out, ref_lse, f"step path {name}")
+    f_out, f_lse = ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"])
+    torch.cuda.synchronize()
+    assert_close(out_acc, lse_acc, f_out.cpu().double().numpy(), f_lse.cpu().double().numpy(),
+                 f"step vs forward {name}")
+
+
+def test_merge_api_and_empty_identity(ra):
+    """ringattn_merge of two forward partials (disjoint key halves) equals the
+    forward over all keys; a partial with lse = -inf and NaN output is the
+    identity; two empties stay (0, -inf)."""
+    x = workload_inputs("flux")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    sc = x["scale"]
+    a_out, a_lse = ra.forward(q, k[:, :2304].contiguous(), v[:, :2304].contiguous(), scale=sc)
+    b_out, b_lse = ra.forward(q, k[:, 2304:].contiguous(), v[:, 2304:].contiguous(), scale=sc)
+    ra.merge(a_out, a_lse, b_out, b_lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = workload_oracle("flux")
+    assert_close(a_out, a_lse, ref_out, ref_lse, "merge api")
+    keep_out, keep_lse = a_out.clone(), a_lse.clone()
+    junk_out = torch.full_like(a_out, float("nan"))
+    junk_lse = torch.full_like(a_lse, float("-inf"))
+    ra.merge(a_out, a_lse, junk_out, junk_lse)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out, keep_out) and torch.equal(a_lse, keep_lse)
+    e_out, e_lse = ra.new_accumulators(q)
+    ra.merge(e_out, e_lse, junk_out.clone(), junk_lse.clone())
+    torch.cuda.synchronize()
+    assert torch.all(e_out == 0) and torch.all(e_lse == float("-inf"))
+    ra.merge(e_out, e_lse, keep_out, keep_lse)
+    torch.cuda.synchronize()
+    assert torch.equal(e_out, keep_out) and torch.equal(e_lse, keep_lse)
+
+
+def test_ring_anything_padded_buffer(ra):
+    """Ring Anything's padded all-gather buffer (every chunk padded to 577 rows,
+    padding filled with large garbage) gives the same result as the packed
+    chunks: padding rows are excluded, never read as zeros."""
+    x = workload_inputs("ring_anything")
+    w = x["workload"]
+    offs = oracle.chunk_offsets(w.seq_len, w.n_chunks, True)
+    pad = oracle.padded_chunk_length(w.seq_len, w.n_chunks)
+    B, S, H, D = x["k"].shape
+    kp = torch.full((B, w.n_chunks * pad, H, D), 300.0, dtype=torch.bfloat16)
+    vp = torch.full((B, w.n_chunks * pad, H, D), -300.0, dtype=torch.bfloat16)
+    for c in range(w.n_chunks):
+        n = offs[c + 1] - offs[c]
+        kp[:, c * pad:c * pad + n] = x["k"][:, offs[c]:offs[c + 1]]
+        vp[:, c * pad:c * pad + n] = x["v"][:, offs[c]:offs[c + 1]]
+    out, lse = ra.forward(dev(x["q"]), dev(kp), dev(vp), chunk_offsets=offs, kv_chunk_stride=pad, scale=x["scale"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = workload_oracle("ring_anything")
+    assert_close(out, lse, ref_out, ref_lse, "padded ring anything")
+
+
+RAGGED_CASES = [
+    # (B, H, D, Sq, chunk lengths, seed)
+    (1, 1, 64, 1, [1], 100),
+    (2, 3, 64, 77, [0, 33, 129, 1, 64, 65], 101),
+    (1, 2, 128, 129, [200, 0, 0, 7], 102),
+    (2, 1, 128, 300, [63, 64, 65, 127, 128, 129], 103),
+    (1, 4, 128, 256, [1000], 104),
+    (3, 2, 64, 45, [17] * 16, 105),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_CASES, ids=lambda c: f"B{c[0]}H{c[1]}D{c[2]}Sq{c[3]}n{len(c[4])}")
+def test_ragged_shapes(ra, case):
+    """Ragged query tails, ragged and empty chunks, both head dims, several
+    batches, vs the oracle; also through the step path."""
+    B, H, D, Sq, lens, seed = case
+    S = sum(lens)
+    x = W.make_random(B, Sq, S, H, D, seed, k_outlier_frac=0.05, k_outlier_scale=5.0)
+    offs = [0]
+    for n in lens:
+        offs.append(offs[-1] + n)
+    print(f"case ragged {case}", flush=True)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    ref_out, ref_lse = oracle.attention_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]), x["scale"])
+    for splits in (0, 1, 5):
+        out, lse = ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=splits)
+        torch.cuda.synchronize()
+        assert_close(out, lse, ref_out, ref_lse, f"ragged forward splits={splits}")
+    out_acc, lse_acc = ra.new_accumulators(q)
+    for c in range(len(lens)):
+        ra.step(q, k[:, offs[c]:offs[c + 1]].contiguous(), v[:, offs[c]:offs[c + 1]].contiguous(),
+                out_acc, lse_acc, scale=x["scale"])
+    torch.cuda.synchronize()
+    assert_close(out_acc, lse_acc, ref_out, ref_lse, "ragged step path")
+
+
+def test_no_keys_gives_empty_result(ra):
+    x = W.make_random(1, 40, 0, 2, 64, 7)
+    q = dev(x["q"])
+    k = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda:0")
+    out, lse = ra.forward(q, k, k.clone(), chunk_offsets=[0, 0, 0], scale=x["scale"])
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(lse == float("-inf"))
+
+
+def test_chunk_order_invariance(ra):
+    """Reordering the chunks (a rank-rotated ring order) changes the result only
+    by rounding."""
+    x = workload_inputs("ring_anything")
+    w = x["workload"]
+    offs = oracle.chunk_offsets(w.seq_len, w.n_chunks, True)
+    order = [3, 4, 5, 6, 7, 0, 1, 2]
+    k = torch.cat([x["k"][:, offs[c]:offs[c + 1]] for c in order], dim=1)
+    v = torch.cat([x["v"][:, offs[c]:offs[c + 1]] for c in order], dim=1)
+    new_offs = [0]
+    for c in order:
+        new_offs.append(new_offs[-1] + offs[c + 1] - offs[c])
+    out, lse = ra.forward(dev(x["q"]), dev(k), dev(v), chunk_offsets=new_offs, scale=x["scale"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = workload_oracle("ring_anything")
+    assert_close(out, lse, ref_out, ref_lse, "rotated chunk order")
+
+
+def test_deterministic(ra):
+    """No atomics: repeated runs are bitwise identical (single split and split)."""
+    x = workload_inputs("ring_anything")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    for splits in (1, 4):
+        a = ra.forward(q, k, v, ring_degree=8, ring_anything=True, scale=x["scale"], n_splits=splits)
+        b = ra.forward(q, k, v, ring_degree=8, ring_anything=True, scale=x["scale"], n_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def sampled_rows(n_rows, count, extra=(), seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(int(r) for r in rng.choice(n_rows, size=min(count, n_rows), replace=False))
+    rows.update([0, n_rows - 1])
+    rows.update(int(r) for r in extra if 0 <= r < n_rows)
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["ulysses", "video"])
+def test_full_size_sampled(ra, name):
+    """The full-size Ulysses share and video shard, run exactly as the benchmark
+    runs them (library partition, automatic plan), compared on sampled query
+    rows (all heads) including the outlier rows of the local shard."""
+    x = W.make_inputs(name)
+    w = x["workload"]
+    print(f"case full-size {name}: q{tuple(x['q'].shape)} kv{tuple(x['k'].shape)}", flush=True)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    out, lse = ra.forward(q, k, v, ring_degree=w.n_chunks, ring_anything=w.ring_anything, scale=x["scale"])
+    torch.cuda.synchronize()
+    rows = sampled_rows(w.q_rows, 24, extra=x["q_outlier_rows"][:8], seed=w.seed)
+    ref_out, ref_lse = oracle.attention_rows_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]),
+                                                  x["scale"], rows)
+    assert_close(out[:, rows], lse[:, :, rows], ref_out, ref_lse, f"{name} sampled rows {len(rows)}")
