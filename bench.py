@@ -41,7 +41,25 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time spent timing the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (calibrates the HBM byte "
+                         "counters of a profiler run) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    """A plain copy kernel of known size: reads and writes mib MiB once."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}),
+          flush=True)
 
 
 def traffic_from_profiles(workload: str):
@@ -97,6 +115,9 @@ def cpu_baseline(x, target_s: float):
 
 def main():
     args = parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's ring shard only; this build has no multi-GPU path "

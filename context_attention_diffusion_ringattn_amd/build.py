@@ -29,6 +29,7 @@ COMMON_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    "-fno-honor-nans",  # scores are finite or -inf, never NaN: lets fmaxf skip NaN canonicalisation
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE,
     "-I", CSRC,

@@ -21,27 +21,36 @@
 //    j(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3), which makes each lane half hold
 //    16 consecutive keys: lane half h, accumulator element v <-> key 16h + v.
 //  * Q lives in registers for the whole sweep (B operand of S^T).
-//  * K tiles are stored row-major in LDS with a 16-byte-granular XOR swizzle
-//    so the A-operand reads (16 bytes per lane) are bank-conflict free.
-//  * V tiles are transposed on their way into LDS (4 rows x 8 columns per
-//    thread, repacked in registers) so the A operand of O^T = V^T P^T is one
-//    16-byte LDS read per lane, also XOR-swizzled.
-//  * Two LDS stages: the global loads of tile t+1 are issued before the MFMAs
-//    of tile t and written to the other stage after them; one barrier per tile.
+//  * K and V tiles go from HBM/L2 straight into LDS with global_load_lds_dwordx4
+//    (no VGPR staging), row-major, 16-byte pieces XOR-swizzled per row.  Each
+//    wave-wide load writes 1 KiB of LDS linearly by lane, so the swizzle is
+//    applied on the global side: lane p of a row fetches the piece that must
+//    live at position p.
+//  * The K operand is one 16-byte LDS read per lane.  The V^T operand is read
+//    with ds_read_b64_tr_b16, which transposes a 4-key x 16-column block per
+//    16-lane group, so V needs no transpose on its way into LDS.
+//  * Two LDS stages: the loads of tile t+1 are issued before the MFMAs of tile
+//    t; one barrier per tile.  The loop is unrolled by two so every LDS offset
+//    is an immediate.
 //  * Workgroups are renumbered so consecutive (q-tile, head) work lands on the
 //    same XCD and shares that XCD's L2 for the head's K/V.
 #include "kernels.h"
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace ringattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kXcds = 8;
 
@@ -53,22 +62,42 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
     return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
 }
 
-// K tile: row-major [64][D] bf16, 16-byte piece `ch` of row `row` stored at
-// piece ch ^ k_swizzle(row).  For the rows one A-operand read touches
-// together (lanes 0..15 read keys 0..3, 16..19, 4..7, 20..23) the swizzle is a
-// bijection onto distinct pieces.
 template <int D>
-__device__ __forceinline__ int k_swizzle(int row) {
+struct Geo {
+    static constexpr int ROW = D * 2;                        // bytes per K/V row in LDS
+    static constexpr int KCH = D / 8;                        // 16-byte pieces per row
+    static constexpr int TILE = kBlockN * ROW;               // bytes of one K (or V) tile
+    static constexpr int STAGE = 2 * TILE;                   // K tile then V tile
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW;         // rows one wave-wide 16-byte load fills
+    static constexpr int LOADS_PER_WAVE = TILE / 1024 / 4;   // per tensor per tile, 4 waves
+    static_assert(LOADS_PER_WAVE * 4 * 1024 == TILE, "tile split over waves");
+};
+
+// K tile swizzle: piece c of row r is stored at c ^ k_swizzle(r).  A K-operand
+// read has 16 lanes in flight reading keys {0..3, 16..19, 4..7, 20..23} (+32)
+// at the same piece; the swizzle sends them to 16 distinct 16-byte bank
+// groups (64 banks x 4 bytes).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int r) {
     if constexpr (D == 128) {
-        return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
-    } else {
-        return (row & 3) | (((row >> 4) & 1) << 2);
+        return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 1) << 3);
+    } else {  // 128-byte rows: two rows share one 256-byte bank window
+        return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 4) & 1) << 2);
     }
 }
 
-// V^T tile: row-major [D][64] bf16 (128 bytes per d-row, 8 pieces of 8 keys),
-// piece p of row d stored at p ^ v_swizzle(d).
-__device__ __forceinline__ int v_swizzle(int d) { return (d ^ (d >> 3)) & 7; }
+// V tile swizzle: a transposing read has 32 lanes in flight covering rows
+// j0..j0+3 (j0 % 4 == 0) and 4 consecutive pieces; XOR on piece bits 2..3
+// (D=128) or bit 2 (D=64, two rows per bank window) spreads them over
+// distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+    if constexpr (D == 128) {
+        return 4 * (r & 3);
+    } else {
+        return 4 * ((r >> 1) & 1);
+    }
+}
 
 // Key index of S^T row m (see header comment).
 __device__ __forceinline__ int key_of_row(int m) {
@@ -84,19 +113,23 @@ __device__ __forceinline__ void tile_info(const ChunkTable &ct, int t, int &c, i
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ bf16x8 lds_read_b128(const unsigned char *smem, int off) {
+    return *(const bf16x8 *)(smem + off);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const unsigned char *smem, int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(smem + off));
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnArgs a) {
-    constexpr int KCH = D / 8;                               // 16-byte pieces per K row
-    constexpr int K_BYTES = kBlockN * D * 2;
-    constexpr int V_BYTES = D * kBlockN * 2;
-    constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int K_PER_THREAD = kBlockN * KCH / kThreads;   // 4 (D=128) or 2 (D=64)
-    constexpr int V_UNITS = (kBlockN / 4) * KCH;             // 4-row x 8-column units
-    static_assert(K_PER_THREAD * kThreads == kBlockN * KCH, "K tile split");
-    static_assert(V_UNITS <= kThreads, "V tile split");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    using G = Geo<D>;
+    // Two separate LDS objects (not one array) so the compiler can tell that
+    // the transposing reads of one stage never alias the in-flight direct
+    // loads into the other, and does not wait for those loads early.
+    __shared__ __attribute__((aligned(1024))) unsigned char stage0[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage1[G::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,8 +149,9 @@ void attn_fwd_kernel(const AttnArgs a) {
     const int t_hi = (int)((int64_t)(split + 1) * a.ct.n_tiles / a.n_splits);
 
     const int64_t HD = (int64_t)a.heads * D;
-    const uint16_t *kbase = a.k + (int64_t)b * a.kv_rows * HD + (int64_t)h * D;
-    const uint16_t *vbase = a.v + (int64_t)b * a.kv_rows * HD + (int64_t)h * D;
+    const uint32_t row_stride = (uint32_t)(HD * 2);  // bytes between consecutive K/V rows
+    const unsigned char *kbase = (const unsigned char *)(a.k + (int64_t)b * a.kv_rows * HD + (int64_t)h * D);
+    const unsigned char *vbase = (const unsigned char *)(a.v + (int64_t)b * a.kv_rows * HD + (int64_t)h * D);
 
     // ---- Q operand (registers for the whole sweep) --------------------------
     const int64_t qrow = (int64_t)qt * kBlockM + wave * 32 + col;
@@ -127,58 +161,61 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
 
-    // ---- global -> register staging of one K/V tile -----------------------
-    u32x4 kst[K_PER_THREAD];
-    u32x4 vst[4];
-    const bool v_active = tid < V_UNITS;
-    const int v_dc = tid % KCH;  // 8-column group of d
-    const int v_jg = tid / KCH;  // 4-row group of keys
+    // ---- per-lane constants of the direct global->LDS loads ---------------
+    // Load i of this wave fills tile rows [r0, r0 + ROWS_PER_LOAD); lane -> row
+    // r0 + lane / KCH at LDS piece lane % KCH.
+    int ld_row[G::LOADS_PER_WAVE];
+    int ld_kpiece[G::LOADS_PER_WAVE];
+    int ld_vpiece[G::LOADS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < G::LOADS_PER_WAVE; ++i) {
+        const int r = (wave * G::LOADS_PER_WAVE + i) * G::ROWS_PER_LOAD + lane / G::KCH;
+        const int p = lane % G::KCH;
+        ld_row[i] = r;
+        ld_kpiece[i] = (p ^ k_swizzle<D>(r)) * 16;
+        ld_vpiece[i] = (p ^ v_swizzle<D>(r)) * 16;
+    }
 
-    auto load_tile = [&](int64_t row0, int nv) {
+    auto issue_loads = [&](int t, int &c, auto stage_tag) {
+        int64_t row0;
+        int nv;
+        tile_info(a.ct, t, c, row0, nv);
+        const unsigned char *kt = kbase + row0 * (int64_t)row_stride;
+        const unsigned char *vt = vbase + row0 * (int64_t)row_stride;
+        unsigned char *kdst = decltype(stage_tag)::value ? stage1 : stage0;
+        unsigned char *vdst = kdst + G::TILE;
 #pragma unroll
-        for (int r = 0; r < K_PER_THREAD; ++r) {
-            const int idx = tid + r * kThreads;
-            const int row = idx / KCH, ch = idx % KCH;
-            kst[r] = u32x4{0u, 0u, 0u, 0u};
-            if (row < nv) kst[r] = *(const u32x4 *)(kbase + (row0 + row) * HD + ch * 8);
-        }
-        if (v_active) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 4 * v_jg + e;
-                vst[e] = u32x4{0u, 0u, 0u, 0u};
-                if (row < nv) vst[e] = *(const u32x4 *)(vbase + (row0 + row) * HD + v_dc * 8);
-            }
+        for (int i = 0; i < G::LOADS_PER_WAVE; ++i) {
+            // rows past the chunk's end re-read its last row: finite data that
+            // the softmax masks (K) or weights by exactly zero (V)
+            const uint32_t rr = (uint32_t)min(ld_row[i], nv - 1) * row_stride;
+            const int lds_off = (wave * G::LOADS_PER_WAVE + i) * 1024;
+            __builtin_amdgcn_global_load_lds((const void *)(kt + rr + ld_kpiece[i]), (lds_void *)(kdst + lds_off), 16,
+                                             0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vt + rr + ld_vpiece[i]), (lds_void *)(vdst + lds_off), 16,
+                                             0, 0);
         }
     };
 
-    auto store_tile = [&](unsigned char *stage) {
-        unsigned char *Ks = stage;
-        unsigned char *Vs = stage + K_BYTES;
+    // ---- per-lane LDS read offsets ------------------------------------------
+    // K operand: row key_of_row(col) (+32 for the second key block), piece
+    // 2*st + half.
+    const int krow = key_of_row(col);
+    int koff[D / 16];
 #pragma unroll
-        for (int r = 0; r < K_PER_THREAD; ++r) {
-            const int idx = tid + r * kThreads;
-            const int row = idx / KCH, ch = idx % KCH;
-            *(u32x4 *)(Ks + row * (D * 2) + ((ch ^ k_swizzle<D>(row)) << 4)) = kst[r];
-        }
-        if (v_active) {
+    for (int st = 0; st < D / 16; ++st) koff[st] = krow * G::ROW + (((2 * st + half) ^ k_swizzle<D>(krow)) << 4);
+    // V^T operand via transposing reads: lane s of 16-lane group g reads row
+    // j0 + s/4 at columns d0 + 4*(s%4) .. +3, d0 = 32*db + 16*(g%2); the group
+    // then holds columns d0 .. d0+15 of rows j0 .. j0+3, one column per lane.
+    const int s16 = lane & 15;
+    const int grp = lane >> 4;
+    int voff[D / 32];
 #pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                const int k = dd >> 1;
-                uint32_t lo, hi;
-                if (dd & 1) {  // odd column: high halves
-                    lo = (vst[0][k] >> 16) | (vst[1][k] & 0xffff0000u);
-                    hi = (vst[2][k] >> 16) | (vst[3][k] & 0xffff0000u);
-                } else {       // even column: low halves
-                    lo = (vst[0][k] & 0xffffu) | (vst[1][k] << 16);
-                    hi = (vst[2][k] & 0xffffu) | (vst[3][k] << 16);
-                }
-                const int d = v_dc * 8 + dd;
-                *(u32x2 *)(Vs + d * (kBlockN * 2) + (((v_jg >> 1) ^ v_swizzle(d)) << 4) + ((v_jg & 1) << 3)) =
-                    u32x2{lo, hi};
-            }
-        }
-    };
+    for (int db = 0; db < D / 32; ++db) {
+        const int r = 16 * half + (s16 >> 2);
+        const int piece = 4 * db + 2 * (grp & 1) + ((s16 & 3) >> 1);
+        voff[db] = G::TILE + r * G::ROW + ((piece ^ v_swizzle<D>(r)) << 4) + ((s16 & 1) << 3);
+    }
 
     // ---- sweep --------------------------------------------------------------
     f32x16 o[D / 32];
@@ -187,62 +224,39 @@ void attn_fwd_kernel(const AttnArgs a) {
     float m_run = -INFINITY;  // running row max of the raw scores q.k
     float l_part = 0.f;       // this lane's share of the running row sum
     const float sl2 = a.scale_log2e;
-
     int c_cmp = 0, c_ld = 0;
-    if (t_lo < t_hi) {
-        int64_t r0;
+
+    auto compute_tile = [&](auto stage_tag, int t) {
+        const unsigned char *smem = decltype(stage_tag)::value ? stage1 : stage0;
+        constexpr int SOFF = 0;
+        int64_t row0_unused;
         int nv;
-        tile_info(a.ct, t_lo, c_ld, r0, nv);
-        load_tile(r0, nv);
-        store_tile(smem);
-    }
-    __syncthreads();
+        tile_info(a.ct, t, c_cmp, row0_unused, nv);
 
-    for (int t = t_lo; t < t_hi; ++t) {
-        const int stage = (t - t_lo) & 1;
-        int64_t r0_cur;
-        int nv_cur;
-        tile_info(a.ct, t, c_cmp, r0_cur, nv_cur);
-        const bool has_next = t + 1 < t_hi;
-        if (has_next) {
-            int64_t r0n;
-            int nvn;
-            tile_info(a.ct, t + 1, c_ld, r0n, nvn);
-            load_tile(r0n, nvn);
-        }
-        const unsigned char *Ks = smem + stage * STAGE;
-        const unsigned char *Vs = Ks + K_BYTES;
-
-        // S^T = K Q^T: two 32-key blocks
-        f32x16 s[2];
+        // S^T = K Q^T for two 32-key blocks, interleaved so the two
+        // accumulation chains hide each other's latency
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            s[jb] = f32x16{};
-            const int jr = 32 * jb + key_of_row(col);
-            const unsigned char *krow = Ks + jr * (D * 2);
-            const int sw = k_swizzle<D>(jr);
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                const bf16x8 kop = *(const bf16x8 *)(krow + (((2 * st + half) ^ sw) << 4));
-                s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[st], s[jb], 0, 0, 0);
-            }
+        for (int st = 0; st < D / 16; ++st) {
+            const bf16x8 k0 = lds_read_b128(smem, koff[st] + SOFF);
+            const bf16x8 k1 = lds_read_b128(smem, koff[st] + SOFF + 32 * G::ROW);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[st], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], s1, 0, 0, 0);
         }
 
         // ragged chunk tail: keys past the chunk's true length get -inf
-        if (nv_cur < kBlockN) {
+        if (nv < kBlockN) {
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    if (32 * jb + 16 * half + v >= nv_cur) s[jb][v] = -INFINITY;
+            for (int v = 0; v < 16; ++v) {
+                if (16 * half + v >= nv) s0[v] = -INFINITY;
+                if (32 + 16 * half + v >= nv) s1[v] = -INFINITY;
+            }
         }
 
         // online softmax
-        float mx = s[0][0];
+        float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[jb][v]);
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         if (__any(m_new > m_run)) {  // wave-uniform: rescale only when a row max moved
@@ -255,40 +269,52 @@ void attn_fwd_kernel(const AttnArgs a) {
         const float mc = m_run * sl2;
         bf16x8 pb[4];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p = fast_exp2(fmaf(s[jb][8 * tt + e], sl2, -mc));
-                    l_part += p;
-                    pb[2 * jb + tt][e] = (__bf16)p;
-                }
-            }
+        for (int e = 0; e < 8; ++e) {
+            const float p0 = fast_exp2(fmaf(s0[e], sl2, -mc));
+            const float p1 = fast_exp2(fmaf(s0[8 + e], sl2, -mc));
+            const float p2 = fast_exp2(fmaf(s1[e], sl2, -mc));
+            const float p3 = fast_exp2(fmaf(s1[8 + e], sl2, -mc));
+            l_part += (p0 + p1) + (p2 + p3);
+            pb[0][e] = (__bf16)p0;
+            pb[1][e] = (__bf16)p1;
+            pb[2][e] = (__bf16)p2;
+            pb[3][e] = (__bf16)p3;
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T; step st covers keys 32*(st>>1) + 16*half + 8*(st&1) + 0..7
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const int d = 32 * db + col;
-            const unsigned char *vrow = Vs + d * (kBlockN * 2);
-            const int sw = v_swizzle(d);
+        for (int st = 0; st < 4; ++st) {
+            const int jrow = 32 * (st >> 1) + 8 * (st & 1);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int piece = 4 * (st >> 1) + 2 * half + (st & 1);
-                const bf16x8 vop = *(const bf16x8 *)(vrow + ((piece ^ sw) << 4));
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[st], o[db], 0, 0, 0);
+            for (int db = 0; db < D / 32; ++db) {
+                const s16x4 lo = lds_read_tr(smem, voff[db] + SOFF + jrow * G::ROW);
+                const s16x4 hi = lds_read_tr(smem, voff[db] + SOFF + (jrow + 4) * G::ROW);
+                const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[st], o[db], 0, 0,
+                                                                 0);
             }
         }
+    };
 
-        if (has_next) store_tile(smem + (stage ^ 1) * STAGE);
+    const int n_t = t_hi - t_lo;
+    constexpr std::integral_constant<int, 0> kStage0{};
+    constexpr std::integral_constant<int, 1> kStage1{};
+    if (n_t > 0) issue_loads(t_lo, c_ld, kStage0);
+    __syncthreads();
+    for (int t = t_lo; t < t_hi; t += 2) {
+        if (t + 1 < t_hi) issue_loads(t + 1, c_ld, kStage1);
+        compute_tile(kStage0, t);
+        __syncthreads();
+        if (t + 1 >= t_hi) break;
+        if (t + 2 < t_hi) issue_loads(t + 2, c_ld, kStage0);
+        compute_tile(kStage1, t + 1);
         __syncthreads();
     }
 
     // ---- epilogue -------------------------------------------------------------
     const float l_tot = l_part + __shfl_xor(l_part, 32);
     if (qrow >= a.q_len) return;
-    const bool any_keys = t_hi > t_lo;
+    const bool any_keys = n_t > 0;
     if (MODE == kModeAccum && !any_keys) return;
 
     float *orow = a.out + ((int64_t)b * a.q_len + qrow) * HD + (int64_t)h * D + 4 * half;
