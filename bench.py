@@ -38,6 +38,8 @@ def parse_args():
     ap.add_argument("--workload", default="video",
                     help="tiny | flux | ring_anything | ulysses | video (default: video)")
     ap.add_argument("--splits", type=int, default=0, help="force the K/V split count (0 = library plan)")
+    ap.add_argument("--block-m", type=int, default=0, help="force query rows per workgroup, 128 or 256 "
+                                                            "(0 = library plan)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time spent timing the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -138,14 +140,14 @@ def main():
     w = x["workload"]
     q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
     offs = ra.chunk_offsets(w.seq_len, w.n_chunks, w.ring_anything)
-    n_splits, ws_bytes = ra.forward_plan(tuple(q.shape), offs, args.splits)
+    n_splits, block_m, ws_bytes = ra.forward_plan(tuple(q.shape), offs, args.splits, args.block_m)
     out = torch.empty((w.batch, w.q_rows, w.heads, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((w.batch, w.heads, w.q_rows), dtype=torch.float32, device=dev)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step():
-        ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=args.splits, out=out, lse=lse,
-                   workspace=ws)
+        ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=n_splits, block_m=block_m, out=out,
+                   lse=lse, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -190,6 +192,7 @@ def main():
             "ring_anything": w.ring_anything,
             "flops_per_step": flops,
             "splits": n_splits,
+            "block_m": block_m,
         },
         "roofline": {
             "bound": "mfma",

@@ -45,6 +45,14 @@ class Shape(ctypes.Structure):
     ]
 
 
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("n_splits", ctypes.c_int32),
+        ("block_m", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
 class RingAttnError(RuntimeError):
     """A library call returned a non-OK status."""
 
@@ -63,6 +71,7 @@ _i64 = ctypes.c_int64
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 _shape_p = ctypes.POINTER(Shape)
+_plan_p = ctypes.POINTER(Plan)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 
 _SIGNATURES = {
@@ -73,9 +82,8 @@ _SIGNATURES = {
     "ringattn_acc_init": (ctypes.c_int, [_vp, _vp, _shape_p, _vp]),
     "ringattn_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _shape_p, _vp]),
     "ringattn_merge": (ctypes.c_int, [_vp, _vp, _vp, _vp, _shape_p, _vp]),
-    "ringattn_forward_plan": (ctypes.c_int, [_shape_p, _i64p, _i32, _i32, ctypes.POINTER(_i32),
-                                             ctypes.POINTER(_sz)]),
-    "ringattn_forward": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _i32, _vp,
+    "ringattn_forward_plan": (ctypes.c_int, [_shape_p, _i64p, _i32, _i64, _plan_p]),
+    "ringattn_forward": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _plan_p, _vp,
                                         _sz, _vp]),
 }
 

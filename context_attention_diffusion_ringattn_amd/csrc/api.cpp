@@ -20,7 +20,7 @@ using namespace ringattn;
 
 static_assert(kMaxChunks == RINGATTN_MAX_CHUNKS, "chunk limit mismatch");
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 thread_local std::string g_last_error;
 
@@ -89,9 +89,17 @@ int cu_count_for_current_device() {
     return cache[dev];
 }
 
-// Fill the chunk table from host offsets; validates the offsets.
-int build_chunk_table(const int64_t *offsets, int32_t n_chunks, int64_t stride, int64_t kv_len, ChunkTable *ct,
-                      int64_t *kv_rows) {
+// The K/V layout of one call, as the kernels walk it.
+struct Layout {
+    ChunkTable ct;
+    int64_t kv_rows;  // rows per batch in the k / v buffers
+    bool chunked;     // tiles follow the chunk table (padded layout)
+};
+
+// Validate host offsets and build the tile walk.  Packed chunks are one
+// contiguous key range, so they become a single table entry and tiles may
+// span chunk boundaries; the padded layout keeps one entry per chunk.
+int build_layout(const int64_t *offsets, int32_t n_chunks, int64_t stride, int64_t kv_len, Layout *L) {
     if (!offsets) return fail(RINGATTN_EINVAL, "chunk_offsets is NULL");
     if (n_chunks < 1 || n_chunks > kMaxChunks)
         return fail(RINGATTN_EINVAL, "n_chunks %d outside [1, %d]", n_chunks, kMaxChunks);
@@ -100,9 +108,6 @@ int build_chunk_table(const int64_t *offsets, int32_t n_chunks, int64_t stride, 
     if (offsets[n_chunks] != kv_len)
         return fail(RINGATTN_EINVAL, "chunk_offsets[%d] = %lld must equal kv_len %lld", n_chunks,
                     (long long)offsets[n_chunks], (long long)kv_len);
-    std::memset(ct, 0, sizeof *ct);
-    ct->n_chunks = n_chunks;
-    int64_t tiles = 0;
     for (int c = 0; c < n_chunks; ++c) {
         const int64_t len = offsets[c + 1] - offsets[c];
         if (len < 0) return fail(RINGATTN_EINVAL, "chunk_offsets decrease at %d", c);
@@ -110,6 +115,23 @@ int build_chunk_table(const int64_t *offsets, int32_t n_chunks, int64_t stride, 
             return fail(RINGATTN_EINVAL, "chunk %d length %lld exceeds kv_chunk_stride %lld", c, (long long)len,
                         (long long)stride);
         if (len > (int64_t)INT32_MAX - kBlockN) return fail(RINGATTN_EINVAL, "chunk %d too long", c);
+    }
+    ChunkTable *ct = &L->ct;
+    std::memset(ct, 0, sizeof *ct);
+    L->chunked = stride > 0 || kv_len > (int64_t)INT32_MAX - kBlockN;
+    L->kv_rows = stride > 0 ? (int64_t)n_chunks * stride : kv_len;
+    if (!L->chunked) {
+        ct->n_chunks = 1;
+        ct->row_start[0] = 0;
+        ct->len[0] = (int32_t)kv_len;
+        ct->tile_start[0] = 0;
+        ct->tile_start[1] = ct->n_tiles = (int32_t)((kv_len + kBlockN - 1) / kBlockN);
+        return RINGATTN_OK;
+    }
+    ct->n_chunks = n_chunks;
+    int64_t tiles = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t len = offsets[c + 1] - offsets[c];
         ct->row_start[c] = stride > 0 ? (int64_t)c * stride : offsets[c];
         ct->len[c] = (int32_t)len;
         ct->tile_start[c] = (int32_t)tiles;
@@ -118,11 +140,11 @@ int build_chunk_table(const int64_t *offsets, int32_t n_chunks, int64_t stride, 
     }
     ct->tile_start[n_chunks] = (int32_t)tiles;
     ct->n_tiles = (int32_t)tiles;
-    *kv_rows = stride > 0 ? (int64_t)n_chunks * stride : kv_len;
     return RINGATTN_OK;
 }
 
 struct Plan {
+    int32_t block_m;
     int32_t n_qtiles;
     int32_t n_splits;
     size_t ws_bytes;
@@ -130,41 +152,53 @@ struct Plan {
     int64_t split_lse_stride;
 };
 
-// Pick the number of K/V splits.  Cost model in units of one workgroup-tile
-// (128 query rows x 64 keys): workgroups run in rounds of `slots` (two
-// resident per CU), a split of T tiles costs ceil(T / s) per workgroup, and
-// s > 1 adds the float32 partial traffic (written once, read once by the
-// merge) at HBM speed.  The constants are measured-order estimates for
-// MI355X: ~1.7 us per workgroup-tile, ~5 TB/s effective HBM.
-int choose_splits(const ringattn_shape *s, int32_t n_tiles, int32_t n_qtiles, int32_t requested) {
-    if (n_tiles <= 1) return 1;
-    const int32_t cap = n_tiles < kMaxSplits ? n_tiles : kMaxSplits;
-    if (requested > 0) return requested < cap ? requested : cap;
-    const double slots = 2.0 * cu_count_for_current_device();
-    const double base = (double)n_qtiles * s->heads * s->batch;
-    const double part_bytes = (double)s->batch * s->q_len * s->heads * (s->head_dim + 1) * 4.0;
-    const double tile_us = 1.7, bytes_per_us = 5.0e6;
-    int best = 1;
-    double best_cost = 1e300;
-    for (int sp = 1; sp <= cap; ++sp) {
-        const double rounds = std::ceil(base * sp / slots);
-        const double per_wg = std::ceil((double)n_tiles / sp);
-        double cost = rounds * per_wg * tile_us;
-        if (sp > 1) cost += (2.0 * sp * part_bytes + part_bytes) / bytes_per_us;
-        if (cost < best_cost * 0.999) {
-            best_cost = cost;
-            best = sp;
-        }
+// Cost model of one launch, in microseconds.  Workgroups run in rounds of
+// `slots` (two 4-wave workgroups or one 8-wave workgroup per CU); a
+// workgroup costs its tile count times the time one tile takes when every
+// CU is busy, plus a fixed start/finish cost; K/V splits add the float32
+// partial traffic (written once, read once by the merge) at HBM speed.  The
+// constants are measured-order estimates for MI355X.
+double plan_cost(const ringattn_shape *s, int32_t n_tiles, int block_m, int splits) {
+    const double cus = cu_count_for_current_device();
+    const double slots = block_m == 256 ? cus : 2.0 * cus;
+    const double tile_us = block_m == 256 ? 1.45 : 2.2;  // one 64-key tile of one workgroup
+    const double fixed_us = 3.0;
+    const double n_qtiles = std::ceil((double)s->q_len / block_m);
+    const double base = n_qtiles * s->heads * s->batch;
+    const double rounds = std::ceil(base * splits / slots);
+    const double per_wg = std::ceil((double)n_tiles / splits);
+    double cost = rounds * (per_wg * tile_us + fixed_us);
+    if (splits > 1) {
+        const double part_bytes = (double)s->batch * s->q_len * s->heads * (s->head_dim + 1) * 4.0;
+        cost += (2.0 * splits * part_bytes + part_bytes) / 5.0e6 + 4.0;
     }
-    return best;
+    return cost;
 }
 
-int make_plan(const ringattn_shape *s, const ChunkTable &ct, int32_t requested, Plan *p) {
-    if (requested < 0) return fail(RINGATTN_EINVAL, "requested_splits must be >= 0");
-    const int64_t n_qtiles = (s->q_len + kBlockM - 1) / kBlockM;
+int make_plan(const ringattn_shape *s, const ChunkTable &ct, int32_t req_splits, int32_t req_block_m, Plan *p) {
+    if (req_splits < 0) return fail(RINGATTN_EINVAL, "requested n_splits must be >= 0");
+    if (req_block_m != 0 && req_block_m != 128 && req_block_m != 256)
+        return fail(RINGATTN_EINVAL, "block_m must be 0 (choose), 128 or 256 (got %d)", req_block_m);
+    const int32_t cap = ct.n_tiles < 1 ? 1 : (ct.n_tiles < kMaxSplits ? ct.n_tiles : kMaxSplits);
+    double best = 1e300;
+    p->block_m = 0;
+    p->n_splits = 1;
+    for (int bm : {256, 128}) {
+        if (req_block_m != 0 && bm != req_block_m) continue;
+        const int lo = req_splits > 0 ? (req_splits < cap ? req_splits : cap) : 1;
+        const int hi = req_splits > 0 ? lo : cap;
+        for (int sp = lo; sp <= hi; ++sp) {
+            const double c = plan_cost(s, ct.n_tiles, bm, sp);
+            if (c < best * 0.999) {
+                best = c;
+                p->block_m = bm;
+                p->n_splits = sp;
+            }
+        }
+    }
+    const int64_t n_qtiles = (s->q_len + p->block_m - 1) / p->block_m;
     if (n_qtiles > INT32_MAX) return fail(RINGATTN_EINVAL, "q_len too large");
     p->n_qtiles = (int32_t)n_qtiles;
-    p->n_splits = choose_splits(s, ct.n_tiles, p->n_qtiles, requested);
     const int64_t grid = n_qtiles * s->heads * s->batch * (int64_t)p->n_splits;
     if (grid > INT32_MAX) return fail(RINGATTN_EINVAL, "grid too large (%lld workgroups)", (long long)grid);
     p->split_out_stride = (int64_t)s->batch * s->q_len * s->heads * s->head_dim;
@@ -174,6 +208,12 @@ int make_plan(const ringattn_shape *s, const ChunkTable &ct, int32_t requested, 
     // keep the lse slots 16-byte aligned after the out slots
     if (p->n_splits > 1) p->ws_bytes += 16;
     return RINGATTN_OK;
+}
+
+hipError_t launch_plan(const AttnArgs &a, const Plan &p, int head_dim, EpilogueMode mode, bool chunked,
+                       hipStream_t s) {
+    if (p.block_m == 256) return launch_attn_pp(a, head_dim, mode, chunked, s);
+    return launch_attn(a, head_dim, mode, s);
 }
 
 void fill_common(AttnArgs *a, const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,
@@ -247,22 +287,24 @@ int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_
     if ((st = check_ptr(q, 16, "q"))) return st;
     if ((st = check_ptr(out_acc, 16, "out_acc"))) return st;
     if ((st = check_ptr(lse_acc, 4, "lse_acc"))) return st;
-    if (!std::isfinite(scale)) return fail(RINGATTN_EINVAL, "scale must be finite");
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(RINGATTN_EINVAL, "scale must be finite and > 0");
     if (shape->kv_len == 0) return ok();  // an empty chunk is the merge identity
     if ((st = check_ptr(k_chunk, 16, "k_chunk"))) return st;
     if ((st = check_ptr(v_chunk, 16, "v_chunk"))) return st;
     AttnArgs a;
     std::memset(&a, 0, sizeof a);
-    int64_t kv_rows = 0;
+    Layout L;
     const int64_t offs[2] = {0, shape->kv_len};
-    if ((st = build_chunk_table(offs, 1, 0, shape->kv_len, &a.ct, &kv_rows))) return st;
+    if ((st = build_layout(offs, 1, 0, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, a.ct, 1, &p))) return st;
+    if ((st = make_plan(shape, L.ct, 1, 0, &p))) return st;
     fill_common(&a, q, k_chunk, v_chunk, out_acc, lse_acc, scale, shape);
-    a.kv_rows = kv_rows;
+    a.ct = L.ct;
+    a.kv_rows = L.kv_rows;
     a.n_qtiles = p.n_qtiles;
     a.n_splits = 1;
-    return check_hip(launch_attn(a, shape->head_dim, kModeAccum, (hipStream_t)stream), "attention launch");
+    return check_hip(launch_plan(a, p, shape->head_dim, kModeAccum, L.chunked, (hipStream_t)stream),
+                     "attention launch");
 }
 
 int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
@@ -279,36 +321,37 @@ int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const 
 }
 
 int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offsets, int32_t n_chunks,
-                          int32_t requested_splits, int32_t *n_splits_out, size_t *workspace_bytes_out) {
+                          int64_t kv_chunk_stride, ringattn_plan *plan) {
     int st;
     if ((st = check_shape(shape, true))) return st;
-    ChunkTable ct;
-    int64_t kv_rows = 0;
-    if ((st = build_chunk_table(chunk_offsets, n_chunks, 0, shape->kv_len, &ct, &kv_rows))) return st;
+    if (!plan) return fail(RINGATTN_EINVAL, "plan is NULL");
+    Layout L;
+    if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, ct, requested_splits, &p))) return st;
-    if (n_splits_out) *n_splits_out = p.n_splits;
-    if (workspace_bytes_out) *workspace_bytes_out = p.ws_bytes;
+    if ((st = make_plan(shape, L.ct, plan->n_splits, plan->block_m, &p))) return st;
+    plan->n_splits = p.n_splits;
+    plan->block_m = p.block_m;
+    plan->workspace_bytes = p.ws_bytes;
     return ok();
 }
 
 int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
                      int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
-                     const ringattn_shape *shape, int32_t requested_splits, void *workspace, size_t workspace_bytes,
+                     const ringattn_shape *shape, const ringattn_plan *plan, void *workspace, size_t workspace_bytes,
                      void *stream) {
     int st;
     if ((st = check_shape(shape, true))) return st;
     if ((st = check_ptr(q, 16, "q"))) return st;
     if ((st = check_ptr(out, 16, "out"))) return st;
     if ((st = check_ptr(lse, 4, "lse"))) return st;
-    if (!std::isfinite(scale)) return fail(RINGATTN_EINVAL, "scale must be finite");
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(RINGATTN_EINVAL, "scale must be finite and > 0");
     AttnArgs a;
     std::memset(&a, 0, sizeof a);
-    int64_t kv_rows = 0;
-    if ((st = build_chunk_table(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &a.ct, &kv_rows)))
-        return st;
+    Layout L;
+    if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, a.ct, requested_splits, &p))) return st;
+    if ((st = make_plan(shape, L.ct, plan ? plan->n_splits : 0, plan ? plan->block_m : 0, &p))) return st;
+    a.ct = L.ct;
     if (a.ct.n_tiles > 0) {
         if ((st = check_ptr(k, 16, "k"))) return st;
         if ((st = check_ptr(v, 16, "v"))) return st;
@@ -326,10 +369,11 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
         return check_hip(launch_acc_init(out, lse, n_out, n_lse, s), "acc_init launch");
     }
     fill_common(&a, q, k, v, out, lse, scale, shape);
-    a.kv_rows = kv_rows;
+    a.kv_rows = L.kv_rows;
     a.n_qtiles = p.n_qtiles;
     a.n_splits = p.n_splits;
-    if (p.n_splits == 1) return check_hip(launch_attn(a, shape->head_dim, kModeFinal, s), "attention launch");
+    if (p.n_splits == 1)
+        return check_hip(launch_plan(a, p, shape->head_dim, kModeFinal, L.chunked, s), "attention launch");
 
     float *part_out = static_cast<float *>(workspace);
     uintptr_t lse_addr = reinterpret_cast<uintptr_t>(part_out + (size_t)p.n_splits * p.split_out_stride);
@@ -339,7 +383,8 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     a.lse = part_lse;
     a.split_out_stride = p.split_out_stride;
     a.split_lse_stride = p.split_lse_stride;
-    if ((st = check_hip(launch_attn(a, shape->head_dim, kModePartial, s), "attention launch"))) return st;
+    if ((st = check_hip(launch_plan(a, p, shape->head_dim, kModePartial, L.chunked, s), "attention launch")))
+        return st;
     MergeSplitsArgs m;
     m.part_out = part_out;
     m.part_lse = part_lse;

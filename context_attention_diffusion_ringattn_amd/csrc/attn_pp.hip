@@ -1,0 +1,436 @@
+// attn_pp.hip -- 8-wave ping-pong ring-shard attention kernel for gfx950.
+//
+// Same computation as attn_fwd.hip (one non-causal softmax-attention sweep of
+// a query block over K/V tiles, the running float32 (max, sum, output) state
+// being the log-sum-exp merge of the partials seen so far -- context
+// parallelism guide "Paralelisme konteks", section "Ring Attention";
+// Parallelism API page, ContextParallelConfig.convert_to_fp32), organised for
+// large query shards:
+//
+//  * One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
+//    owns 32 rows.  Every K/V tile brought into LDS is used by all 256 rows.
+//  * Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs pairwise and
+//    run the same loop one phase apart.  A wave alternates an MFMA phase
+//    (O^T += V^T P^T for tile t-1, then S^T = K Q^T for tile t) and a softmax
+//    phase (tile t).  While group A issues MFMAs, group B does its softmax on
+//    the VALU, and the other way round; workgroup barriers separate the
+//    phases and the MFMA phase runs at raised wave priority so the matrix
+//    pipe is fed first.
+//  * K/V tiles stream through a ring of four LDS stages by direct
+//    global->LDS loads, issued two tiles ahead; each wave waits only for its
+//    own loads of the next tile before the barrier that publishes it.
+//  * Softmax: row max by max3 + one cross-half lane swap; O and the row sum
+//    are rescaled only when some row's max moved (wave-uniform branch).  The
+//    running max is kept exact, so the largest probability of a row is
+//    exactly 1 and its bf16 rounding in the PV product is exact -- with a
+//    peaked softmax that one term carries the row.
+//  * Packed K/V (one contiguous key range) needs no chunk table in the loop;
+//    the padded Ring Anything buffer (chunks at a fixed stride) walks the
+//    chunk table and never lets a tile straddle two chunks.
+#include "attn_tiles.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace ringattn {
+namespace {
+
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = 64 * kPPWaves;
+constexpr int kPPBlockM = 32 * kPPWaves;  // 256 query rows per workgroup
+
+template <int D>
+struct PPGeo {
+    static constexpr int ROW = D * 2;                    // bytes per K/V row
+    static constexpr int KCH = D / 8;                    // 16-byte pieces per row
+    static constexpr int TILE = kBlockN * ROW;           // bytes of one K (or V) tile
+    static constexpr int STAGE = 2 * TILE;               // K tile then V tile
+    static constexpr int RPL = 1024 / ROW;               // rows one wave-wide 16-byte load fills
+    static constexpr int LPW = TILE / 1024 / kPPWaves;   // loads per wave, per tensor, per tile
+    static constexpr int VM_PER_TILE = 2 * LPW;          // vmcnt events per wave per tile
+    static_assert(LPW >= 1 && LPW * kPPWaves * 1024 == TILE, "tile split over waves");
+};
+
+// Workgroup barrier that neither the compiler's scheduler nor its memory
+// optimisations move anything across, and that (unlike __syncthreads) does
+// not wait for the in-flight global->LDS loads of later tiles.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The value of lane i ^ 32 (the other half of the wave).
+// v_permlane32_swap_b32 exchanges the upper 32 lanes of its first operand
+// with the lower 32 lanes of its second: for inputs (a, b) it leaves
+// a' = [a_lo, b_lo] and b' = [a_hi, b_hi]; with a = b = x, lane i then holds
+// x[i ^ 32] in b' (lower lanes) or a' (upper lanes).  It is issued as inline
+// assembly because the compiler's builtin folding drops one of the two
+// results when they feed a floating-point max or add.  The s_nop pairs cover
+// the VALU-write -> permlane-read hazard before and the permlane-write ->
+// VALU-read hazard after, which the hazard recognizer cannot see through
+// inline assembly.
+__device__ __forceinline__ float other_half(float x, bool upper) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return upper ? a : b;
+}
+
+template <int D, int MODE, bool CHUNKED>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_pp_kernel(const AttnArgs a) {
+    using G = PPGeo<D>;
+    // Four LDS stages as separate objects, so that the compiler can tell a
+    // read of one stage from the in-flight direct loads into another.
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[G::STAGE];
+    auto stage = [&](auto s) __attribute__((always_inline)) -> unsigned char * {
+        constexpr int S = decltype(s)::value;
+        if constexpr (S == 0) return st0;
+        else if constexpr (S == 1) return st1;
+        else if constexpr (S == 2) return st2;
+        else return st3;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;   // 0: leads, 1: trails by one phase
+    const int col = lane & 31;   // query row within the wave's 32 rows
+    const int half = lane >> 5;  // which 32-lane half
+
+    // ---- work assignment ------------------------------------------------
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = w % a.n_qtiles;
+    w /= a.n_qtiles;
+    const int h = w % a.heads;
+    w /= a.heads;
+    const int b = w % a.batch;
+    const int split = w / a.batch;
+    const int t_lo = (int)((int64_t)split * a.ct.n_tiles / a.n_splits);
+    const int t_hi = (int)((int64_t)(split + 1) * a.ct.n_tiles / a.n_splits);
+    const int T = t_hi - t_lo;
+    const int len0 = a.ct.len[0];  // packed layout: the whole key range
+
+    const int64_t HD = (int64_t)a.heads * D;
+    const uint32_t row_stride = (uint32_t)(HD * 2);  // bytes between consecutive K/V rows
+    const unsigned char *kbase = (const unsigned char *)(a.k + (int64_t)b * a.kv_rows * HD + (int64_t)h * D);
+    const unsigned char *vbase = (const unsigned char *)(a.v + (int64_t)b * a.kv_rows * HD + (int64_t)h * D);
+
+    int c_ld = 0, c_sm = 0;  // chunk cursors of the two tile walks (chunked layout)
+    auto tile_at = [&](int t, int &c, int64_t &row0, int &nv) __attribute__((always_inline)) {
+        if constexpr (CHUNKED) {
+            tile_info(a.ct, t, c, row0, nv);
+        } else {
+            row0 = (int64_t)t * kBlockN;
+            nv = min(kBlockN, len0 - t * kBlockN);
+        }
+    };
+
+    // ---- Q operand (registers for the whole sweep) --------------------------
+    const int64_t qrow = (int64_t)qt * kPPBlockM + wave * 32 + col;
+    const int64_t qrow_ld = qrow < a.q_len ? qrow : a.q_len - 1;
+    const uint16_t *qp = a.q + ((int64_t)b * a.q_len + qrow_ld) * HD + (int64_t)h * D + 8 * half;
+    bf16x8 qreg[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
+
+    // ---- per-lane constants of the direct global->LDS loads ---------------
+    // Load i of this wave fills tile rows [r0, r0 + RPL); lane -> row
+    // r0 + lane / KCH at LDS piece lane % KCH, fetched from the swizzled piece.
+    int ld_row[G::LPW];
+    uint32_t ld_k[G::LPW], ld_v[G::LPW];
+#pragma unroll
+    for (int i = 0; i < G::LPW; ++i) {
+        const int r = (wave * G::LPW + i) * G::RPL + lane / G::KCH;
+        const int p = lane % G::KCH;
+        ld_row[i] = r;
+        ld_k[i] = (uint32_t)r * row_stride + (uint32_t)((p ^ k_swizzle<D>(r)) * 16);
+        ld_v[i] = (uint32_t)r * row_stride + (uint32_t)((p ^ v_swizzle<D>(r)) * 16);
+    }
+    const int lds_slot = wave * G::LPW * 1024;
+
+    auto issue_loads = [&](auto s, int t) __attribute__((always_inline)) {
+        int64_t row0;
+        int nv;
+        tile_at(t, c_ld, row0, nv);
+        const unsigned char *kt = kbase + row0 * (int64_t)row_stride;
+        const unsigned char *vt = vbase + row0 * (int64_t)row_stride;
+        unsigned char *dst = stage(s) + lds_slot;
+#pragma unroll
+        for (int i = 0; i < G::LPW; ++i) {
+            uint32_t ok = ld_k[i], ov = ld_v[i];
+            if (nv < kBlockN) {
+                // rows past the tile's valid rows re-read its last valid row:
+                // finite data that the softmax masks (K) or weights by zero (V)
+                const uint32_t back = (uint32_t)(ld_row[i] - min(ld_row[i], nv - 1)) * row_stride;
+                ok -= back;
+                ov -= back;
+            }
+            __builtin_amdgcn_global_load_lds((const void *)(kt + ok), (lds_void *)(dst + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vt + ov), (lds_void *)(dst + G::TILE + i * 1024), 16, 0,
+                                             0);
+        }
+    };
+
+    // ---- per-lane LDS read offsets ------------------------------------------
+    const int krow = key_of_row(col);
+    int koff[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) koff[st] = krow * G::ROW + (((2 * st + half) ^ k_swizzle<D>(krow)) << 4);
+    // V^T operand via transposing reads: lane s of 16-lane group g reads row
+    // j0 + s/4 at columns d0 + 4*(s%4) .. +3, d0 = 32*db + 16*(g%2); the group
+    // then holds columns d0 .. d0+15 of rows j0 .. j0+3, one column per lane.
+    const int s16 = lane & 15;
+    const int g16 = lane >> 4;
+    int voff[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int r = 16 * half + (s16 >> 2);
+        const int piece = 4 * db + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+        voff[db] = G::TILE + r * G::ROW + ((piece ^ v_swizzle<D>(r)) << 4) + ((s16 & 1) << 3);
+    }
+
+    // ---- sweep state --------------------------------------------------------
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    bf16x8 pb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = bf16x8{};
+    float m_run = -INFINITY;                 // running row max of the raw scores q.k
+    float l0 = 0.f, l1 = 0.f, l2 = 0.f, l3 = 0.f;  // this lane's share of the running row sum
+    const float sl2 = a.scale_log2e;
+
+    // S^T = K Q^T for the tile in stage s: two 32-key blocks, interleaved.
+    auto qk = [&](auto s) __attribute__((always_inline)) {
+        const unsigned char *sm = stage(s);
+        s0 = f32x16{};
+        s1 = f32x16{};
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            const bf16x8 k0 = lds_read_b128(sm, koff[st]);
+            const bf16x8 k1 = lds_read_b128(sm, koff[st] + 32 * G::ROW);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[st], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], s1, 0, 0, 0);
+        }
+    };
+
+    // O^T += V^T P^T for the tile in stage s; step st covers keys
+    // 32*(st>>1) + 16*half + 8*(st&1) + 0..7.
+    auto pv = [&](auto s) __attribute__((always_inline)) {
+        const unsigned char *sm = stage(s);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int jrow = 32 * (st >> 1) + 8 * (st & 1);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const s16x4 lo = lds_read_tr(sm, voff[db] + jrow * G::ROW);
+                const s16x4 hi = lds_read_tr(sm, voff[db] + (jrow + 4) * G::ROW);
+                const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[st], o[db], 0, 0,
+                                                                 0);
+            }
+        }
+    };
+
+    // Online softmax of the scores of tile t (in s0, s1) -> probabilities pb.
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+        int64_t row0_unused;
+        int nv;
+        tile_at(t, c_sm, row0_unused, nv);
+        if (nv < kBlockN) {  // ragged tile: keys past the valid rows get -inf
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if (16 * half + v >= nv) s0[v] = -INFINITY;
+                if (32 + 16 * half + v >= nv) s1[v] = -INFINITY;
+            }
+        }
+        // two independent max3 chains, one per 32-key block
+        float ma = fmaxf(s0[0], s0[1]);
+        float mb = fmaxf(s1[0], s1[1]);
+#pragma unroll
+        for (int v = 2; v < 16; v += 2) {
+            ma = fmaxf(fmaxf(ma, s0[v]), s0[v + 1]);
+            mb = fmaxf(fmaxf(mb, s1[v]), s1[v + 1]);
+        }
+        float mx = fmaxf(ma, mb);
+        mx = fmaxf(mx, other_half(mx, half != 0));
+        if (__any(mx > m_run)) {  // wave-uniform; rare once the row maxima settle
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2((m_run - m_new) * sl2);
+            l0 *= alpha;
+            l1 *= alpha;
+            l2 *= alpha;
+            l3 *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+            m_run = m_new;
+        }
+        const float mc = m_run * sl2;
+        // the row sum is taken over the float32 probabilities: with a peaked
+        // softmax one term dominates it, and its bf16 rounding (2^-9
+        // relative) would go straight into the LSE
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p0 = fast_exp2(fmaf(s0[e], sl2, -mc));
+            const float p1 = fast_exp2(fmaf(s0[8 + e], sl2, -mc));
+            const float p2 = fast_exp2(fmaf(s1[e], sl2, -mc));
+            const float p3 = fast_exp2(fmaf(s1[8 + e], sl2, -mc));
+            l0 += p0;
+            l1 += p1;
+            l2 += p2;
+            l3 += p3;
+            pb[0][e] = (__bf16)p0;
+            pb[1][e] = (__bf16)p1;
+            pb[2][e] = (__bf16)p2;
+            pb[3][e] = (__bf16)p3;
+        }
+    };
+
+    // ---- ping-pong sweep ------------------------------------------------------
+    // Tile j lives in stage j % 4.  Its loads are issued in the MFMA phase of
+    // step j-2 and waited for (per wave) before the barrier that precedes the
+    // first read of K(j); V(j) is last read in the MFMA phase of step j+1, by
+    // group B, before group A issues the loads of tile j+4 into the same stage.
+    constexpr std::integral_constant<int, 0> I0{};
+    constexpr std::integral_constant<int, 1> I1{};
+    constexpr std::integral_constant<int, 2> I2{};
+    constexpr std::integral_constant<int, 3> I3{};
+    if (T > 0) issue_loads(I0, t_lo);
+    if (T > 1) issue_loads(I1, t_lo + 1);
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (grp == 1) wg_barrier();
+
+    auto step = [&](auto jc, int j) __attribute__((always_inline)) -> bool {
+        constexpr int J = decltype(jc)::value;
+        constexpr std::integral_constant<int, J> SK{};
+        constexpr std::integral_constant<int, (J + 3) % 4> SV{};
+        constexpr std::integral_constant<int, (J + 2) % 4> SL{};
+        // MFMA phase
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        if (j + 2 < T) issue_loads(SL, t_lo + j + 2);
+        if (j >= 1) pv(SV);
+        if (j < T) qk(SK);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        if (j >= T) return false;
+        if (grp == 1) {
+            if (j + 2 < T) wait_vmcnt<G::VM_PER_TILE>();
+            else wait_vmcnt<0>();
+        }
+        wg_barrier();
+        // softmax phase
+        softmax(t_lo + j);
+        if (grp == 0) {
+            if (j + 2 < T) wait_vmcnt<G::VM_PER_TILE>();
+            else wait_vmcnt<0>();
+        }
+        wg_barrier();
+        return true;
+    };
+    for (int j = 0;; j += 4) {
+        if (!step(I0, j)) break;
+        if (!step(I1, j + 1)) break;
+        if (!step(I2, j + 2)) break;
+        if (!step(I3, j + 3)) break;
+    }
+    if (grp == 0) wg_barrier();  // both groups pass the same number of barriers
+
+    // ---- epilogue -------------------------------------------------------------
+    const float l_lane = (l0 + l1) + (l2 + l3);
+    const float l_tot = l_lane + other_half(l_lane, half != 0);
+    if (qrow >= a.q_len) return;
+    const bool any_keys = T > 0;
+    if (MODE == kModeAccum && !any_keys) return;
+
+    float *orow = a.out + ((int64_t)b * a.q_len + qrow) * HD + (int64_t)h * D + 4 * half;
+    float *lptr = a.lse + ((int64_t)b * a.heads + h) * a.q_len + qrow;
+    if (MODE == kModePartial) {
+        orow += (int64_t)split * a.split_out_stride;
+        lptr += (int64_t)split * a.split_lse_stride;
+    }
+    const float inv_l = any_keys ? 1.f / l_tot : 0.f;
+    const float lse_chunk = any_keys ? fmaf(m_run, a.scale, logf(l_tot)) : -INFINITY;
+
+    if (MODE == kModeAccum) {
+        const float la = *lptr;
+        float wa, wb, lse_new;
+        if (la == -INFINITY) {
+            wa = 0.f;
+            wb = 1.f;
+            lse_new = lse_chunk;
+        } else {
+            lse_new = fmaxf(la, lse_chunk) + log1pf(expf(-fabsf(la - lse_chunk)));
+            wa = expf(la - lse_new);
+            wb = expf(lse_chunk - lse_new);
+        }
+        wb *= inv_l;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 *p = (f32x4 *)(orow + 32 * db + 8 * g);
+                const f32x4 cur = f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                f32x4 res = cur * wb;
+                if (la != -INFINITY) res += wa * (*p);
+                *p = res;
+            }
+        }
+        if (half == 0) *lptr = lse_new;
+    } else {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                *(f32x4 *)(orow + 32 * db + 8 * g) =
+                    f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]} * inv_l;
+            }
+        }
+        if (half == 0) *lptr = lse_chunk;
+    }
+}
+
+template <int D, bool CHUNKED>
+hipError_t launch_pp_dc(const AttnArgs &a, EpilogueMode mode, hipStream_t stream) {
+    const int64_t grid = (int64_t)a.n_qtiles * a.heads * a.batch * a.n_splits;
+    switch (mode) {
+        case kModeFinal:
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModeFinal, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+                               stream, a);
+            break;
+        case kModePartial:
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModePartial, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+                               stream, a);
+            break;
+        case kModeAccum:
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModeAccum, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+                               stream, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_pp(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream) {
+    if (head_dim == 128) return chunked ? launch_pp_dc<128, true>(a, mode, stream) : launch_pp_dc<128, false>(a, mode, stream);
+    return chunked ? launch_pp_dc<64, true>(a, mode, stream) : launch_pp_dc<64, false>(a, mode, stream);
+}
+
+}  // namespace ringattn

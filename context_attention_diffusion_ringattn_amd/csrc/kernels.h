@@ -63,6 +63,8 @@ struct MergeSplitsArgs {
 };
 
 hipError_t launch_attn(const AttnArgs &a, int head_dim, EpilogueMode mode, hipStream_t stream);
+// 8-wave, 256-row variant; `chunked` = walk the chunk table (padded layout).
+hipError_t launch_attn_pp(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream);
 hipError_t launch_merge_splits(const MergeSplitsArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_merge2(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
                          int64_t q_len, int32_t batch, int32_t heads, int32_t head_dim, hipStream_t stream);

@@ -16,7 +16,7 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import RingAttnError, Shape, check, lib, offsets_array
+from ._lib import Plan, RingAttnError, Shape, check, lib, offsets_array
 
 
 # ------------------------------------------------------------------ config --
@@ -165,16 +165,17 @@ def merge(out_acc: torch.Tensor, lse_acc: torch.Tensor, out_part: torch.Tensor, 
                                ctypes.byref(shape), _stream_handle(out_acc.device, stream)), "ringattn_merge")
 
 
-def forward_plan(q_shape: Sequence[int], offsets: Sequence[int], requested_splits: int = 0) -> Tuple[int, int]:
-    """(n_splits, workspace_bytes) the library will use for a forward call."""
+def forward_plan(q_shape: Sequence[int], offsets: Sequence[int], n_splits: int = 0, block_m: int = 0,
+                 kv_chunk_stride: int = 0) -> Tuple[int, int, int]:
+    """(n_splits, block_m, workspace_bytes) of the plan the library uses for a
+    forward call; n_splits / block_m = 0 let the library choose."""
     B, Sq, H, D = q_shape
     shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=int(offsets[-1]))
-    n = ctypes.c_int32(0)
-    ws = ctypes.c_size_t(0)
+    plan = Plan(n_splits=int(n_splits), block_m=int(block_m), workspace_bytes=0)
     arr = offsets_array(offsets)
-    check(lib().ringattn_forward_plan(ctypes.byref(shape), arr, len(offsets) - 1, int(requested_splits),
-                                      ctypes.byref(n), ctypes.byref(ws)), "ringattn_forward_plan")
-    return n.value, ws.value
+    check(lib().ringattn_forward_plan(ctypes.byref(shape), arr, len(offsets) - 1, int(kv_chunk_stride),
+                                      ctypes.byref(plan)), "ringattn_forward_plan")
+    return plan.n_splits, plan.block_m, plan.workspace_bytes
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
@@ -184,6 +185,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
             kv_chunk_stride: int = 0,
             scale: Optional[float] = None,
             n_splits: int = 0,
+            block_m: int = 0,
             out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None,
@@ -227,17 +229,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     _check_f32(lse, "lse", (B, H, Sq), q.device)
     shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=offs[-1])
     arr = offsets_array(offs)
+    plan = Plan(n_splits=int(n_splits), block_m=int(block_m), workspace_bytes=0)
     if workspace is None:
-        nsp = ctypes.c_int32(0)
-        ws_bytes = ctypes.c_size_t(0)
-        check(lib().ringattn_forward_plan(ctypes.byref(shape), arr, n_chunks, int(n_splits), ctypes.byref(nsp),
-                                          ctypes.byref(ws_bytes)), "ringattn_forward_plan")
-        if ws_bytes.value:
-            workspace = torch.empty((ws_bytes.value,), dtype=torch.uint8, device=q.device)
+        check(lib().ringattn_forward_plan(ctypes.byref(shape), arr, n_chunks, int(kv_chunk_stride),
+                                          ctypes.byref(plan)), "ringattn_forward_plan")
+        if plan.workspace_bytes:
+            workspace = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(lib().ringattn_forward(_ptr(q), _ptr(k), _ptr(v), arr, n_chunks, int(kv_chunk_stride), _ptr(out), _ptr(lse),
-                                 ctypes.c_float(scale), ctypes.byref(shape), int(n_splits), ws_ptr, ws_len,
+                                 ctypes.c_float(scale), ctypes.byref(shape), ctypes.byref(plan), ws_ptr, ws_len,
                                  _stream_handle(q.device, stream)), "ringattn_forward")
     return out, lse
 

@@ -111,7 +111,7 @@ int ringattn_acc_init(float *out_acc, float *lse_acc, const ringattn_shape *shap
  * copied (the old accumulator output is never multiplied).  The merge is
  * fused into the attention kernel's epilogue.  kv_len = 0 is a no-op.
  * Start from ringattn_acc_init; after all N chunks the accumulators hold the
- * shard's attention output and LSE.  scale must be finite.
+ * shard's attention output and LSE.  scale must be finite and > 0.
  */
 int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk,
                   float *out_acc, float *lse_acc, float scale,
@@ -127,16 +127,29 @@ int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const 
                    const ringattn_shape *shape, void *stream);
 
 /*
- * Launch plan of ringattn_forward for these arguments: the number of
- * key/value splits it will use (independent partial passes over disjoint
- * ranges of K/V tiles, merged at the end by their LSE) and the workspace
- * bytes that plan needs (0 when n_splits is 1).
- *   requested_splits = 0: the library picks from the shape and the GPU's
- *     compute-unit count; > 0: use that many (clamped to the K/V tile count).
- * n_splits_out and workspace_bytes_out may each be NULL.
+ * Launch plan of ringattn_forward.
+ *   n_splits: number of key/value splits -- independent partial passes over
+ *     disjoint ranges of K/V tiles, merged at the end by their LSE;
+ *   block_m: query rows per workgroup, 128 (4 waves) or 256 (8 waves in two
+ *     groups that alternate MFMA and softmax phases);
+ *   workspace_bytes: device workspace the plan needs (0 when n_splits is 1).
+ * On input n_splits and block_m are requests (0 = the library chooses from
+ * the shape and the GPU's compute-unit count; n_splits > 0 is clamped to the
+ * K/V tile count); on output they hold what ringattn_forward will use.
+ */
+typedef struct ringattn_plan {
+    int32_t n_splits;
+    int32_t block_m;
+    uint64_t workspace_bytes;
+} ringattn_plan;
+
+/*
+ * Fill *plan (see ringattn_plan) for a ringattn_forward call with these
+ * arguments.  Pure host code: validates like ringattn_forward and launches
+ * nothing.  Plans are deterministic for a given shape, layout and device.
  */
 int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offsets, int32_t n_chunks,
-                          int32_t requested_splits, int32_t *n_splits_out, size_t *workspace_bytes_out);
+                          int64_t kv_chunk_stride, ringattn_plan *plan);
 
 /*
  * The whole shard in one call: q attends to all n_chunks K/V chunks and the
@@ -152,17 +165,20 @@ int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offs
  *     n_chunks * kv_chunk_stride rows per batch and the padding rows are
  *     never read.
  * Chunks are visited in order 0..n_chunks-1 with an online softmax whose
- * running float32 (max, sum, output) state is the LSE merge of the chunk
- * partials so far.  requested_splits as in ringattn_forward_plan; when the
- * plan has more than one split, workspace must hold the planned bytes
- * (RINGATTN_EWORKSPACE otherwise).  workspace may be NULL with
+ * running float32 (max, sum, output) state is the LSE merge of the partials
+ * seen so far; with the packed layout a K/V tile may span the boundary of two
+ * chunks (their rows are contiguous), with the padded layout it never does.
+ * plan: NULL for the library's choice, else the requests of a
+ * ringattn_plan (its workspace_bytes is ignored).  When the plan has more
+ * than one split, workspace must hold the planned bytes
+ * (RINGATTN_EWORKSPACE otherwise); workspace may be NULL with
  * workspace_bytes = 0 only when the plan needs none.  With kv_len = 0 the
  * result is out = 0, lse = -inf.
  */
 int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      const int64_t *chunk_offsets, int32_t n_chunks, int64_t kv_chunk_stride,
                      float *out, float *lse, float scale, const ringattn_shape *shape,
-                     int32_t requested_splits, void *workspace, size_t workspace_bytes, void *stream);
+                     const ringattn_plan *plan, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

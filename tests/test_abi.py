@@ -40,7 +40,7 @@ def test_header_symbols_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ringattn_abi_version() == 1
+    assert L.ringattn_abi_version() == 2
     assert _lib.status_string(0) == "RINGATTN_OK"
     assert _lib.status_string(-1) == "RINGATTN_EINVAL"
     assert _lib.status_string(-2) == "RINGATTN_EUNSUPPORTED"
@@ -115,8 +115,9 @@ def test_step_pointer_errors(L):
     assert L.ringattn_step(P, P, P, P, None, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
     assert L.ringattn_step(P_MISALIGNED, P, P, P, P, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
     assert "aligned" in _lib.last_error()
-    assert L.ringattn_step(P, P, P, P, P, ctypes.c_float(float("inf")), ctypes.byref(s), None) == \
-        _lib.RINGATTN_EINVAL
+    for bad_scale in (float("inf"), float("nan"), 0.0, -0.125):
+        assert L.ringattn_step(P, P, P, P, P, ctypes.c_float(bad_scale), ctypes.byref(s), None) == \
+            _lib.RINGATTN_EINVAL
     assert L.ringattn_step(P, P, P, P, P, f, None, None) == _lib.RINGATTN_EINVAL
 
 
@@ -127,10 +128,17 @@ def test_step_empty_chunk_is_noop(L):
     assert L.ringattn_step(P, None, None, P, P, ctypes.c_float(0.125), ctypes.byref(s), None) == 0
 
 
-def _fwd(L, offs, s, stride=0, splits=0, ws=None, ws_bytes=0, q=P, k=P, v=P, out=P, lse=P, scale=0.125):
+def _fwd(L, offs, s, stride=0, splits=0, block_m=0, ws=None, ws_bytes=0, q=P, k=P, v=P, out=P, lse=P, scale=0.125):
     arr = _lib.offsets_array(offs) if offs is not None else None
+    plan = _lib.Plan(n_splits=splits, block_m=block_m, workspace_bytes=0)
     return L.ringattn_forward(q, k, v, arr, (len(offs) - 1) if offs is not None else 1, stride, out, lse,
-                              ctypes.c_float(scale), ctypes.byref(s), splits, ws, ws_bytes, None)
+                              ctypes.c_float(scale), ctypes.byref(s), ctypes.byref(plan), ws, ws_bytes, None)
+
+
+def _plan(L, s, offs, splits=0, block_m=0, stride=0):
+    plan = _lib.Plan(n_splits=splits, block_m=block_m, workspace_bytes=0)
+    st = L.ringattn_forward_plan(ctypes.byref(s), _lib.offsets_array(offs), len(offs) - 1, stride, ctypes.byref(plan))
+    return st, plan
 
 
 def test_forward_offset_errors(L):
@@ -143,45 +151,59 @@ def test_forward_offset_errors(L):
     assert _fwd(L, [0, 128, 256], s, stride=100) == _lib.RINGATTN_EINVAL  # chunk longer than the stride
     assert _fwd(L, [0, 128, 256], s, stride=-1) == _lib.RINGATTN_EINVAL
     assert _fwd(L, [0, 128, 256], s, splits=-1) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], s, block_m=64) == _lib.RINGATTN_EINVAL
     assert _fwd(L, [0, 128, 256], s, out=P_MISALIGNED) == _lib.RINGATTN_EINVAL
     assert _fwd(L, [0, 128, 256], s, q=None) == _lib.RINGATTN_EINVAL
     assert _fwd(L, [0, 128, 256], s, scale=float("nan")) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], s, scale=0.0) == _lib.RINGATTN_EINVAL
+    assert _fwd(L, [0, 128, 256], s, scale=-0.125) == _lib.RINGATTN_EINVAL
     assert _fwd(L, [0, 128, 256], shape(D=80)) == _lib.RINGATTN_EUNSUPPORTED
 
 
 def test_forward_workspace_error(L):
     """A plan with several splits and no (or too small a) workspace is refused."""
     s = shape(B=1, H=2, D=128, Sq=128, Skv=4096)
-    n = ctypes.c_int32()
-    ws = ctypes.c_size_t()
-    offs = _lib.offsets_array([0, 4096])
-    assert L.ringattn_forward_plan(ctypes.byref(s), offs, 1, 4, ctypes.byref(n), ctypes.byref(ws)) == 0
-    assert n.value == 4 and ws.value >= 4 * (128 * 2 * 128 + 2 * 128) * 4
-    assert _fwd(L, [0, 4096], s, splits=4) == _lib.RINGATTN_EWORKSPACE
-    assert _fwd(L, [0, 4096], s, splits=4, ws=P, ws_bytes=ws.value - 1) == _lib.RINGATTN_EWORKSPACE
-    assert _fwd(L, [0, 4096], s, splits=4, ws=P_MISALIGNED, ws_bytes=ws.value) == _lib.RINGATTN_EINVAL
+    for bm in (128, 256):
+        st, plan = _plan(L, s, [0, 4096], splits=4, block_m=bm)
+        assert st == 0
+        assert plan.n_splits == 4 and plan.block_m == bm
+        assert plan.workspace_bytes >= 4 * (128 * 2 * 128 + 2 * 128) * 4
+        ws = plan.workspace_bytes
+        assert _fwd(L, [0, 4096], s, splits=4, block_m=bm) == _lib.RINGATTN_EWORKSPACE
+        assert _fwd(L, [0, 4096], s, splits=4, block_m=bm, ws=P, ws_bytes=ws - 1) == _lib.RINGATTN_EWORKSPACE
+        assert _fwd(L, [0, 4096], s, splits=4, block_m=bm, ws=P_MISALIGNED, ws_bytes=ws) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_forward_plan(ctypes.byref(s), _lib.offsets_array([0, 4096]), 1, 0, None) == \
+        _lib.RINGATTN_EINVAL
 
 
 def test_forward_plan_properties(L):
     """Plans: a single split needs no workspace; splits never exceed the number
-    of K/V tiles; the plan is deterministic."""
-    for (B, H, D, Sq, offs) in ((1, 24, 128, 8192, oracle.chunk_offsets(65536, 8)),
-                                (1, 24, 128, 1152, oracle.chunk_offsets(4608, 4)),
-                                (1, 24, 128, 577, oracle.chunk_offsets(4611, 8, True)),
-                                (1, 6, 128, 16384, [0, 16384]),
-                                (1, 2, 64, 128, [0, 128, 256]),
-                                (1, 1, 64, 1, [0, 1])):
+    of K/V tiles (packed chunks form one key range, padded chunks are tiled
+    one by one); block_m is 128 or 256; the plan is deterministic and a
+    request for either block size is honoured."""
+    for (B, H, D, Sq, offs, stride) in ((1, 24, 128, 8192, oracle.chunk_offsets(65536, 8), 0),
+                                        (1, 24, 128, 1152, oracle.chunk_offsets(4608, 4), 0),
+                                        (1, 24, 128, 577, oracle.chunk_offsets(4611, 8, True), 0),
+                                        (1, 24, 128, 577, oracle.chunk_offsets(4611, 8, True), 577),
+                                        (1, 6, 128, 16384, [0, 16384], 0),
+                                        (1, 2, 64, 128, [0, 128, 256], 0),
+                                        (1, 1, 64, 1, [0, 1], 0)):
         s = shape(B=B, H=H, D=D, Sq=Sq, Skv=offs[-1])
-        arr = _lib.offsets_array(offs)
-        n = ctypes.c_int32()
-        ws = ctypes.c_size_t()
-        assert L.ringattn_forward_plan(ctypes.byref(s), arr, len(offs) - 1, 0, ctypes.byref(n), ctypes.byref(ws)) == 0
-        tiles = sum(-(-(b - a) // 64) for a, b in zip(offs, offs[1:]))
-        assert 1 <= n.value <= max(1, tiles)
-        assert (ws.value == 0) == (n.value == 1)
-        n2 = ctypes.c_int32()
-        L.ringattn_forward_plan(ctypes.byref(s), arr, len(offs) - 1, 0, ctypes.byref(n2), None)
-        assert n2.value == n.value
+        st, plan = _plan(L, s, offs, stride=stride)
+        assert st == 0
+        if stride:
+            tiles = sum(-(-(b - a) // 64) for a, b in zip(offs, offs[1:]))
+        else:
+            tiles = -(-offs[-1] // 64)
+        assert 1 <= plan.n_splits <= max(1, tiles)
+        assert plan.block_m in (128, 256)
+        assert (plan.workspace_bytes == 0) == (plan.n_splits == 1)
+        st2, plan2 = _plan(L, s, offs, stride=stride)
+        assert (plan2.n_splits, plan2.block_m, plan2.workspace_bytes) == \
+            (plan.n_splits, plan.block_m, plan.workspace_bytes)
+        for bm in (128, 256):
+            st3, plan3 = _plan(L, s, offs, block_m=bm, stride=stride)
+            assert st3 == 0 and plan3.block_m == bm
 
 
 def test_merge_and_init_errors(L):

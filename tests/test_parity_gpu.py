@@ -80,17 +80,18 @@ def test_forward_small_workloads(ra, name):
 
 @pytest.mark.parametrize("name", ["flux", "ring_anything"])
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
-def test_forward_forced_splits(ra, name, splits):
-    """Every split count gives the oracle's result (the split partials are
-    merged by LSE in the merge kernel)."""
+@pytest.mark.parametrize("block_m", [128, 256])
+def test_forward_forced_splits(ra, name, splits, block_m):
+    """Every split count and both workgroup shapes give the oracle's result
+    (the split partials are merged by LSE in the merge kernel)."""
     x = workload_inputs(name)
     w = x["workload"]
-    print(f"case {name} splits={splits}", flush=True)
+    print(f"case {name} splits={splits} block_m={block_m}", flush=True)
     out, lse = ra.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]), ring_degree=w.n_chunks,
-                          ring_anything=w.ring_anything, scale=x["scale"], n_splits=splits)
+                          ring_anything=w.ring_anything, scale=x["scale"], n_splits=splits, block_m=block_m)
     torch.cuda.synchronize()
     ref_out, ref_lse = workload_oracle(name)
-    assert_close(out, lse, ref_out, ref_lse, f"forward {name} splits={splits}")
+    assert_close(out, lse, ref_out, ref_lse, f"forward {name} splits={splits} block_m={block_m}")
 
 
 @pytest.mark.parametrize("name", ["tiny", "flux", "ring_anything"])
@@ -158,10 +159,13 @@ def test_ring_anything_padded_buffer(ra):
         n = offs[c + 1] - offs[c]
         kp[:, c * pad:c * pad + n] = x["k"][:, offs[c]:offs[c + 1]]
         vp[:, c * pad:c * pad + n] = x["v"][:, offs[c]:offs[c + 1]]
-    out, lse = ra.forward(dev(x["q"]), dev(kp), dev(vp), chunk_offsets=offs, kv_chunk_stride=pad, scale=x["scale"])
-    torch.cuda.synchronize()
     ref_out, ref_lse = workload_oracle("ring_anything")
-    assert_close(out, lse, ref_out, ref_lse, "padded ring anything")
+    for block_m in (128, 256):
+        for splits in (0, 3):
+            out, lse = ra.forward(dev(x["q"]), dev(kp), dev(vp), chunk_offsets=offs, kv_chunk_stride=pad,
+                                  scale=x["scale"], n_splits=splits, block_m=block_m)
+            torch.cuda.synchronize()
+            assert_close(out, lse, ref_out, ref_lse, f"padded ring anything block_m={block_m} splits={splits}")
 
 
 RAGGED_CASES = [
@@ -188,10 +192,22 @@ def test_ragged_shapes(ra, case):
     print(f"case ragged {case}", flush=True)
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     ref_out, ref_lse = oracle.attention_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]), x["scale"])
-    for splits in (0, 1, 5):
-        out, lse = ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=splits)
+    for block_m in (128, 256):
+        for splits in (0, 1, 5):
+            out, lse = ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=splits, block_m=block_m)
+            torch.cuda.synchronize()
+            assert_close(out, lse, ref_out, ref_lse, f"ragged forward block_m={block_m} splits={splits}")
+        # the same chunks as a padded buffer (chunk table walked in the kernel)
+        pad = max(max(lens), 1)
+        kp = torch.full((B, len(lens) * pad, H, D), float("nan"), dtype=torch.bfloat16)
+        vp = torch.full((B, len(lens) * pad, H, D), float("nan"), dtype=torch.bfloat16)
+        for c in range(len(lens)):
+            kp[:, c * pad:c * pad + lens[c]] = x["k"][:, offs[c]:offs[c + 1]]
+            vp[:, c * pad:c * pad + lens[c]] = x["v"][:, offs[c]:offs[c + 1]]
+        out, lse = ra.forward(q, dev(kp), dev(vp), chunk_offsets=offs, kv_chunk_stride=pad, scale=x["scale"],
+                              block_m=block_m)
         torch.cuda.synchronize()
-        assert_close(out, lse, ref_out, ref_lse, f"ragged forward splits={splits}")
+        assert_close(out, lse, ref_out, ref_lse, f"ragged padded block_m={block_m}")
     out_acc, lse_acc = ra.new_accumulators(q)
     for c in range(len(lens)):
         ra.step(q, k[:, offs[c]:offs[c + 1]].contiguous(), v[:, offs[c]:offs[c + 1]].contiguous(),
@@ -231,11 +247,14 @@ def test_deterministic(ra):
     """No atomics: repeated runs are bitwise identical (single split and split)."""
     x = workload_inputs("ring_anything")
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    for splits in (1, 4):
-        a = ra.forward(q, k, v, ring_degree=8, ring_anything=True, scale=x["scale"], n_splits=splits)
-        b = ra.forward(q, k, v, ring_degree=8, ring_anything=True, scale=x["scale"], n_splits=splits)
-        torch.cuda.synchronize()
-        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for block_m in (128, 256):
+        for splits in (1, 4):
+            a = ra.forward(q, k, v, ring_degree=8, ring_anything=True, scale=x["scale"], n_splits=splits,
+                           block_m=block_m)
+            b = ra.forward(q, k, v, ring_degree=8, ring_anything=True, scale=x["scale"], n_splits=splits,
+                           block_m=block_m)
+            torch.cuda.synchronize()
+            assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 def sampled_rows(n_rows, count, extra=(), seed=0):
