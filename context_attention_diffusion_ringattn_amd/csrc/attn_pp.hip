@@ -61,6 +61,38 @@ __device__ __forceinline__ void wg_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+
+// A value the compiler cannot see through (no instruction is emitted).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// LDS reads at a lane base address plus a constant offset (folded into the
+// instruction's 16-bit offset field).
+__device__ __forceinline__ bf16x8 lds_b128_at(uint32_t base, uint32_t off) {
+    return *(const bf16x8 *)((const lds_byte *)base + off);
+}
+__device__ __forceinline__ s16x4 lds_tr_at(uint32_t base, uint32_t off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)((lds_byte *)base + off));
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane l's 16 bytes from
+// gbase + voff land at LDS address lds_dst + 16 l (lds_dst wave-uniform, in
+// M0).  Written as inline assembly on purpose: with the builtin in the loop,
+// the compiler treats every LDS read as completing out of order and waits for
+// all of them before each use; hidden from it, the LDS reads get exact
+// counts.  Completion is tracked by vmcnt, which this kernel waits on
+// explicitly before the barrier that publishes a tile.  The "memory" clobber
+// tells the compiler LDS (and anything else) may change here.
+__device__ __forceinline__ void dma_load16(const unsigned char *gbase, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_dst), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -90,19 +122,10 @@ template <int D, int MODE, bool CHUNKED>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pp_kernel(const AttnArgs a) {
     using G = PPGeo<D>;
-    // Four LDS stages as separate objects, so that the compiler can tell a
-    // read of one stage from the in-flight direct loads into another.
-    __shared__ __attribute__((aligned(1024))) unsigned char st0[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st1[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[G::STAGE];
-    auto stage = [&](auto s) __attribute__((always_inline)) -> unsigned char * {
-        constexpr int S = decltype(s)::value;
-        if constexpr (S == 0) return st0;
-        else if constexpr (S == 1) return st1;
-        else if constexpr (S == 2) return st2;
-        else return st3;
-    };
+    // Four LDS stages: V tiles in [0, 4*TILE), K tiles in [4*TILE, 8*TILE).
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * G::TILE];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_byte *)smem;
+    constexpr uint32_t kKRegion = 4 * G::TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -163,12 +186,14 @@ void attn_pp_kernel(const AttnArgs a) {
     const int lds_slot = wave * G::LPW * 1024;
 
     auto issue_loads = [&](auto s, int t) __attribute__((always_inline)) {
+        constexpr uint32_t S = decltype(s)::value;
         int64_t row0;
         int nv;
         tile_at(t, c_ld, row0, nv);
         const unsigned char *kt = kbase + row0 * (int64_t)row_stride;
         const unsigned char *vt = vbase + row0 * (int64_t)row_stride;
-        unsigned char *dst = stage(s) + lds_slot;
+        const uint32_t kdst = lds0 + kKRegion + S * G::TILE + lds_slot;
+        const uint32_t vdst = lds0 + S * G::TILE + lds_slot;
 #pragma unroll
         for (int i = 0; i < G::LPW; ++i) {
             uint32_t ok = ld_k[i], ov = ld_v[i];
@@ -179,28 +204,31 @@ void attn_pp_kernel(const AttnArgs a) {
                 ok -= back;
                 ov -= back;
             }
-            __builtin_amdgcn_global_load_lds((const void *)(kt + ok), (lds_void *)(dst + i * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vt + ov), (lds_void *)(dst + G::TILE + i * 1024), 16, 0,
-                                             0);
+            dma_load16(kt, ok, kdst + i * 1024);
+            dma_load16(vt, ov, vdst + i * 1024);
         }
     };
 
     // ---- per-lane LDS read offsets ------------------------------------------
+    // K operand: row key_of_row(col) (+32 for the second key block), piece
+    // 2*st + half.  The base registers are opaque to the compiler so that the
+    // stage and block offsets become instruction immediates.
     const int krow = key_of_row(col);
-    int koff[D / 16];
+    uint32_t kb[D / 16];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) koff[st] = krow * G::ROW + (((2 * st + half) ^ k_swizzle<D>(krow)) << 4);
+    for (int st = 0; st < D / 16; ++st)
+        kb[st] = opaque(lds0 + kKRegion + krow * G::ROW + (((2 * st + half) ^ k_swizzle<D>(krow)) << 4));
     // V^T operand via transposing reads: lane s of 16-lane group g reads row
     // j0 + s/4 at columns d0 + 4*(s%4) .. +3, d0 = 32*db + 16*(g%2); the group
     // then holds columns d0 .. d0+15 of rows j0 .. j0+3, one column per lane.
     const int s16 = lane & 15;
     const int g16 = lane >> 4;
-    int voff[D / 32];
+    uint32_t vb[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
         const int r = 16 * half + (s16 >> 2);
         const int piece = 4 * db + 2 * (g16 & 1) + ((s16 & 3) >> 1);
-        voff[db] = G::TILE + r * G::ROW + ((piece ^ v_swizzle<D>(r)) << 4) + ((s16 & 1) << 3);
+        vb[db] = opaque(lds0 + r * G::ROW + ((piece ^ v_swizzle<D>(r)) << 4) + ((s16 & 1) << 3));
     }
 
     // ---- sweep state --------------------------------------------------------
@@ -215,35 +243,60 @@ void attn_pp_kernel(const AttnArgs a) {
     float l0 = 0.f, l1 = 0.f, l2 = 0.f, l3 = 0.f;  // this lane's share of the running row sum
     const float sl2 = a.scale_log2e;
 
-    // S^T = K Q^T for the tile in stage s: two 32-key blocks, interleaved.
-    auto qk = [&](auto s) __attribute__((always_inline)) {
-        const unsigned char *sm = stage(s);
-        s0 = f32x16{};
-        s1 = f32x16{};
+    // The MFMA phase: O^T += V^T P^T for the previous tile (V in stage sv)
+    // and S^T = K Q^T for the current one (K in stage sk), as one straight
+    // run of MFMAs.  PV step st covers keys 32*(st>>1) + 16*half + 8*(st&1)
+    // + 0..7; QK uses two 32-key blocks whose accumulation chains interleave.
+    // Each half is scheduled to keep the LDS reads of its next kWin MFMAs
+    // in flight: 2 transposing reads per PV MFMA, 1 read per QK MFMA.
+    auto mfma_phase = [&](auto sv, auto sk, auto do_pv, auto do_qk) __attribute__((always_inline)) {
+        constexpr bool PV = decltype(do_pv)::value;
+        constexpr bool QK = decltype(do_qk)::value;
+        constexpr int kDsRead = 0x100, kMfma = 0x008, kWin = 4;
+        if constexpr (PV) {
+            constexpr uint32_t VS = decltype(sv)::value * G::TILE;
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const bf16x8 k0 = lds_read_b128(sm, koff[st]);
-            const bf16x8 k1 = lds_read_b128(sm, koff[st] + 32 * G::ROW);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], s1, 0, 0, 0);
-        }
-    };
-
-    // O^T += V^T P^T for the tile in stage s; step st covers keys
-    // 32*(st>>1) + 16*half + 8*(st&1) + 0..7.
-    auto pv = [&](auto s) __attribute__((always_inline)) {
-        const unsigned char *sm = stage(s);
+            for (int st = 0; st < 4; ++st) {
+                const int jrow = 32 * (st >> 1) + 8 * (st & 1);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int jrow = 32 * (st >> 1) + 8 * (st & 1);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const s16x4 lo = lds_read_tr(sm, voff[db] + jrow * G::ROW);
-                const s16x4 hi = lds_read_tr(sm, voff[db] + (jrow + 4) * G::ROW);
-                const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[st], o[db], 0, 0,
-                                                                 0);
+                for (int db = 0; db < D / 32; ++db) {
+                    const s16x4 lo = lds_tr_at(vb[db], VS + jrow * G::ROW);
+                    const s16x4 hi = lds_tr_at(vb[db], VS + (jrow + 4) * G::ROW);
+                    const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[st], o[db], 0,
+                                                                     0, 0);
+                }
             }
+            // keep the reads of the next kWin MFMAs in flight
+            constexpr int NPV = 4 * (D / 32);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * kWin, 0);
+#pragma unroll
+            for (int i = 0; i < NPV - kWin; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kMfma, kWin, 0);
+            if constexpr (QK) __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (QK) {
+            constexpr uint32_t KS = decltype(sk)::value * G::TILE;
+            s0 = f32x16{};
+            s1 = f32x16{};
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                const bf16x8 k0 = lds_b128_at(kb[st], KS);
+                const bf16x8 k1 = lds_b128_at(kb[st], KS + 32 * G::ROW);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[st], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], s1, 0, 0, 0);
+            }
+            constexpr int NQK = 2 * (D / 16);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, kWin, 1);
+#pragma unroll
+            for (int i = 0; i < NQK - kWin; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(kMfma, kWin, 1);
         }
     };
 
@@ -253,10 +306,13 @@ void attn_pp_kernel(const AttnArgs a) {
         int nv;
         tile_at(t, c_sm, row0_unused, nv);
         if (nv < kBlockN) {  // ragged tile: keys past the valid rows get -inf
+            // this lane's keys are 16*half + v (block 0) and 32 + 16*half + v
+            const int lim0 = nv - 16 * half;
+            const int lim1 = lim0 - 32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                if (16 * half + v >= nv) s0[v] = -INFINITY;
-                if (32 + 16 * half + v >= nv) s1[v] = -INFINITY;
+                if (v >= lim0) s0[v] = -INFINITY;
+                if (v >= lim1) s1[v] = -INFINITY;
             }
         }
         // two independent max3 chains, one per 32-key block
@@ -302,49 +358,60 @@ void attn_pp_kernel(const AttnArgs a) {
     };
 
     // ---- ping-pong sweep ------------------------------------------------------
-    // Tile j lives in stage j % 4.  Its loads are issued in the MFMA phase of
-    // step j-2 and waited for (per wave) before the barrier that precedes the
-    // first read of K(j); V(j) is last read in the MFMA phase of step j+1, by
-    // group B, before group A issues the loads of tile j+4 into the same stage.
+    // Step j = MFMA phase (PV of tile j-1, QK of tile j) + softmax phase of
+    // tile j; group B runs one phase behind group A.  Tile j lives in stage
+    // j % 4.  Its loads are issued in the MFMA phase of step j-2 and waited
+    // for (per wave) before the barrier that precedes the first read of K(j);
+    // V(j) is last read in the MFMA phase of step j+1, by group B, before
+    // group A issues the loads of tile j+4 into the same stage.  Barriers per
+    // wave: 2 per step + 2 (the trailing group's first, the leading group's
+    // last), for both groups.
     constexpr std::integral_constant<int, 0> I0{};
     constexpr std::integral_constant<int, 1> I1{};
     constexpr std::integral_constant<int, 2> I2{};
     constexpr std::integral_constant<int, 3> I3{};
+    constexpr std::true_type ON{};
+    constexpr std::false_type OFF{};
     if (T > 0) issue_loads(I0, t_lo);
     if (T > 1) issue_loads(I1, t_lo + 1);
     wait_vmcnt<0>();
     wg_barrier();
     if (grp == 1) wg_barrier();
 
-    auto step = [&](auto jc, int j) __attribute__((always_inline)) -> bool {
-        constexpr int J = decltype(jc)::value;
-        constexpr std::integral_constant<int, J> SK{};
-        constexpr std::integral_constant<int, (J + 3) % 4> SV{};
-        constexpr std::integral_constant<int, (J + 2) % 4> SL{};
-        // MFMA phase
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(1);
-        if (j + 2 < T) issue_loads(SL, t_lo + j + 2);
-        if (j >= 1) pv(SV);
-        if (j < T) qk(SK);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
-        if (j >= T) return false;
+    // the softmax phase of step j, with the waits and barriers around it
+    auto softmax_phase = [&](int j) __attribute__((always_inline)) {
         if (grp == 1) {
             if (j + 2 < T) wait_vmcnt<G::VM_PER_TILE>();
             else wait_vmcnt<0>();
         }
         wg_barrier();
-        // softmax phase
         softmax(t_lo + j);
         if (grp == 0) {
             if (j + 2 < T) wait_vmcnt<G::VM_PER_TILE>();
             else wait_vmcnt<0>();
         }
         wg_barrier();
+    };
+    // Step j (j % 4 == J): the MFMA phase -- loads of tile j+2, PV of tile
+    // j-1 (j >= 1), QK of tile j (j < T) -- then, for j < T, the softmax
+    // phase of tile j.  The steady state (both halves) is one straight run.
+    auto step = [&](auto jc, int j) __attribute__((always_inline)) -> bool {
+        constexpr int J = decltype(jc)::value;
+        constexpr std::integral_constant<int, J> SK{};
+        constexpr std::integral_constant<int, (J + 3) % 4> SV{};
+        constexpr std::integral_constant<int, (J + 2) % 4> SL{};
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        if (j + 2 < T) issue_loads(SL, t_lo + j + 2);
+        if (j >= 1) mfma_phase(SV, SK, ON, OFF);
+        if (j < T) mfma_phase(SV, SK, OFF, ON);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        if (j >= T) return false;
+        softmax_phase(j);
         return true;
     };
-    for (int j = 0;; j += 4) {
+    for (int j = 0;; j += 4) {  // unrolled by four so that every stage index is a constant
         if (!step(I0, j)) break;
         if (!step(I1, j + 1)) break;
         if (!step(I2, j + 2)) break;
