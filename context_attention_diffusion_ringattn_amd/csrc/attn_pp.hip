@@ -359,13 +359,15 @@ void attn_pp_kernel(const AttnArgs a) {
 
     // ---- ping-pong sweep ------------------------------------------------------
     // Step j = MFMA phase (PV of tile j-1, QK of tile j) + softmax phase of
-    // tile j; group B runs one phase behind group A.  Tile j lives in stage
-    // j % 4.  Its loads are issued in the MFMA phase of step j-2 and waited
-    // for (per wave) before the barrier that precedes the first read of K(j);
-    // V(j) is last read in the MFMA phase of step j+1, by group B, before
-    // group A issues the loads of tile j+4 into the same stage.  Barriers per
-    // wave: 2 per step + 2 (the trailing group's first, the leading group's
-    // last), for both groups.
+    // tile j; group B runs one phase behind group A, so phase k of the
+    // workgroup is A's step-(k/2) MFMA phase and B's softmax phase, then the
+    // other way round.  Tile j lives in stage j % 4.  Its loads are issued in
+    // the softmax phases of step j-2 (phase 2j-3 by A, 2j-2 by B) and waited
+    // for before the barrier that ends phase 2j-1; K(j) is first read in
+    // phase 2j.  V(j) is last read in phase 2j+3 (B's MFMA phase of step
+    // j+1); the loads of tile j+4 into the same stage are issued from phase
+    // 2j+5 on.  Barriers per wave: 2 per step + 2 (the trailing group's
+    // first, the leading group's last), for both groups.
     constexpr std::integral_constant<int, 0> I0{};
     constexpr std::integral_constant<int, 1> I1{};
     constexpr std::integral_constant<int, 2> I2{};
@@ -378,13 +380,17 @@ void attn_pp_kernel(const AttnArgs a) {
     wg_barrier();
     if (grp == 1) wg_barrier();
 
-    // the softmax phase of step j, with the waits and barriers around it
-    auto softmax_phase = [&](int j) __attribute__((always_inline)) {
-        if (grp == 1) {
-            if (j + 2 < T) wait_vmcnt<G::VM_PER_TILE>();
-            else wait_vmcnt<0>();
-        }
+    // The softmax phase of step j, with the waits and barriers around it.
+    // Each group issues its share of the loads of tile j+2 at the start of
+    // its softmax phase -- never in the MFMA phase, where a stalled
+    // vector-memory issue would idle the matrix pipe.  Before the barrier
+    // that publishes tile j+1, group B (end of its MFMA phase) has no later
+    // loads in flight and waits for all; group A (end of its softmax phase)
+    // may leave the loads of tile j+2 in flight.
+    auto softmax_phase = [&](auto sl, int j) __attribute__((always_inline)) {
+        if (grp == 1) wait_vmcnt<0>();
         wg_barrier();
+        if (j + 2 < T) issue_loads(sl, t_lo + j + 2);
         softmax(t_lo + j);
         if (grp == 0) {
             if (j + 2 < T) wait_vmcnt<G::VM_PER_TILE>();
@@ -392,9 +398,8 @@ void attn_pp_kernel(const AttnArgs a) {
         }
         wg_barrier();
     };
-    // Step j (j % 4 == J): the MFMA phase -- loads of tile j+2, PV of tile
-    // j-1 (j >= 1), QK of tile j (j < T) -- then, for j < T, the softmax
-    // phase of tile j.  The steady state (both halves) is one straight run.
+    // Step j (j % 4 == J): the MFMA phase -- PV of tile j-1 (j >= 1) and QK
+    // of tile j (j < T) -- then, for j < T, the softmax phase of tile j.
     auto step = [&](auto jc, int j) __attribute__((always_inline)) -> bool {
         constexpr int J = decltype(jc)::value;
         constexpr std::integral_constant<int, J> SK{};
@@ -402,13 +407,12 @@ void attn_pp_kernel(const AttnArgs a) {
         constexpr std::integral_constant<int, (J + 2) % 4> SL{};
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
-        if (j + 2 < T) issue_loads(SL, t_lo + j + 2);
         if (j >= 1) mfma_phase(SV, SK, ON, OFF);
         if (j < T) mfma_phase(SV, SK, OFF, ON);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (j >= T) return false;
-        softmax_phase(j);
+        softmax_phase(SL, j);
         return true;
     };
     for (int j = 0;; j += 4) {  // unrolled by four so that every stage index is a constant
