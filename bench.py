@@ -16,6 +16,7 @@ times the fp64 oracle on a bounded sample of query rows on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -64,17 +65,28 @@ def copy_probe(mib: int) -> None:
           flush=True)
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per launch of the attention kernel from committed rocprofv3
-    PMC summaries (profiles/<kernel>_<workload>_traffic.json), or None."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
-    if not os.path.exists(path):
+def traffic_from_profiles(workload: str, block_m: int):
+    """HBM bytes per launch of the attention kernel, from the committed
+    rocprofv3 counter record profiles/attn_pp_<workload>_traffic.json
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size).
+
+    None when there is no record for this workload, when the plan launches a
+    different kernel than the one counted, or when any source the record
+    lists has changed since the counters were taken (its sha256 differs)."""
+    if block_m != 256:
         return None
+    path = os.path.join(ROOT, "profiles", f"attn_pp_{workload}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
-        return rec.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
+        h = hashlib.sha256()
+        for src in rec["kernel_sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["kernel_sources_sha256"]:
+            return None
+        return int(round(rec["hbm_bytes_per_launch"]))
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -100,7 +112,8 @@ def cpu_baseline(x, target_s: float):
         out, lse = oracle.attention_rows_fp64(q64, k64, v64, x["scale"], rows)
         return rows, out, lse, time.perf_counter() - t0
 
-    n0 = min(4, w.q_rows)
+    run(min(2, w.q_rows))                      # BLAS thread pool start-up, page faults
+    n0 = min(8, w.q_rows)
     _, _, _, t0 = run(n0)
     n = int(max(n0, min(w.q_rows, n0 * target_s / max(t0, 1e-3))))
     rows, out, lse, t = run(n)
@@ -170,7 +183,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
 
-    traffic = traffic_from_profiles(args.workload)
+    traffic = traffic_from_profiles(args.workload, block_m)
     result = {
         "metric": METRIC,
         "value": round(value, 2),

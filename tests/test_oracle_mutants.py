@@ -149,3 +149,60 @@ def test_real_oracle_passes_everything():
         check(attention_fp64, lse_merge_fp64, ring_shard_fp64)
     for check in MERGE_ONLY_CHECKS:
         check(attention_fp64, lse_merge_fp64)
+
+
+# ------------------------------------------------------------- offsets ----
+
+def _lengths_mutant(kind):
+    def lengths(S, N, ring_anything=True):
+        if kind == "no_divisibility_check":
+            pass
+        elif not ring_anything and S % N:
+            raise ValueError("not divisible")
+        base, rem = divmod(S, N)
+        if kind == "extra_to_last":
+            return [base + (1 if i >= N - rem else 0) for i in range(N)]
+        if kind == "off_by_one_remainder":
+            return [base + (1 if i < rem + 1 else 0) for i in range(N)]
+        if kind == "remainder_on_last":
+            return [base] * (N - 1) + [base + rem]
+        if kind == "ceil_then_rest":
+            c = -(-S // N)
+            out, left = [], S
+            for _ in range(N):
+                out.append(min(c, left))
+                left -= out[-1]
+            return out
+        return [base + (1 if i < rem else 0) for i in range(N)]
+    return lengths
+
+
+OFFSET_MUTANTS = ["extra_to_last", "off_by_one_remainder", "remainder_on_last", "ceil_then_rest",
+                  "no_divisibility_check"]
+
+
+def _offset_pins_catch(lengths):
+    """The offset pins of test_oracle.py, applied to a candidate lengths rule:
+    numpy.array_split, the 577/576 split of S=4611 over 8, and the pages'
+    divisibility failure at 1008x1008 on 4 GPUs."""
+    for S in range(0, 120):
+        for N in range(1, 11):
+            if lengths(S, N) != [len(p) for p in np.array_split(np.arange(S), N)]:
+                return True
+    if lengths(4611, 8) != [577] * 3 + [576] * 5:
+        return True
+    try:
+        lengths(4481, 4, ring_anything=False)
+    except ValueError:
+        return False
+    return True
+
+
+@pytest.mark.parametrize("kind", OFFSET_MUTANTS)
+def test_offsets_mutant_caught(kind):
+    assert _offset_pins_catch(_lengths_mutant(kind)), f"offsets mutant {kind} passed every offset pin"
+
+
+def test_offset_pins_accept_the_oracle():
+    from oracle import chunk_lengths
+    assert not _offset_pins_catch(lambda S, N, ring_anything=True: chunk_lengths(S, N, ring_anything))
