@@ -3,8 +3,11 @@
 
 A step is one full pass of the shard: the local Q rows attend to every K/V
 chunk and the float32 output + LSE are produced (``ringattn_forward``: all
-chunk passes, the LSE merge and, if planned, the split merge).  Inputs are
-seeded synthetic bf16 tensors already resident in HBM when timing starts.
+chunk passes, the LSE merge and, if planned, the split merge).  With
+``--sweep`` a step is the whole ring on this GPU (``ringattn_ring_sweep``):
+every rank's rows, each rank visiting the chunks in its rotated order with a
+float32 merge per step.  Inputs are seeded synthetic bf16 tensors already
+resident in HBM when timing starts.
 
 Prints ONE JSON line.  ``value`` is attention TFLOP/s = 4*B*Sq*Skv*D*H /
 seconds per step.  ``roofline`` reports the attention kernel against the
@@ -44,6 +47,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate host time spent timing the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the whole ring on this GPU instead of one shard: every rank's query rows, each "
+                         "rank visiting the chunks in its rotated order with a float32 merge per step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the HBM byte "
                          "counters of a profiler run) and exit")
@@ -90,8 +96,8 @@ def traffic_from_profiles(workload: str, block_m: int):
         return None
 
 
-def cpu_baseline(x, target_s: float):
-    """Time the oracle on a sample of local query rows (all heads, all keys)."""
+def cpu_baseline(x, target_s: float, q_key: str = "q"):
+    """Time the oracle on a sample of query rows of x[q_key] (all heads, all keys)."""
     import numpy as np
 
     import oracle
@@ -103,19 +109,20 @@ def cpu_baseline(x, target_s: float):
     except Exception:  # threadpoolctl missing or no BLAS info
         threads = 1
     w = x["workload"]
-    q64, k64, v64 = W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"])
+    q64, k64, v64 = W.to_f64(x[q_key]), W.to_f64(x["k"]), W.to_f64(x["v"])
+    n_rows = q64.shape[1]
     rng = np.random.default_rng(1234)
 
     def run(n):
-        rows = sorted(int(r) for r in rng.choice(w.q_rows, size=min(n, w.q_rows), replace=False))
+        rows = sorted(int(r) for r in rng.choice(n_rows, size=min(n, n_rows), replace=False))
         t0 = time.perf_counter()
         out, lse = oracle.attention_rows_fp64(q64, k64, v64, x["scale"], rows)
         return rows, out, lse, time.perf_counter() - t0
 
-    run(min(2, w.q_rows))                      # BLAS thread pool start-up, page faults
-    n0 = min(8, w.q_rows)
+    run(min(2, n_rows))                        # BLAS thread pool start-up, page faults
+    n0 = min(64, n_rows)
     _, _, _, t0 = run(n0)
-    n = int(max(n0, min(w.q_rows, n0 * target_s / max(t0, 1e-3))))
+    n = int(max(n0, min(n_rows, n0 * target_s / max(t0, 1e-3))))
     rows, out, lse, t = run(n)
     flops = 4.0 * w.batch * len(rows) * w.seq_len * w.head_dim * w.heads
     return {
@@ -123,7 +130,7 @@ def cpu_baseline(x, target_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{len(rows)} of {w.q_rows} local query rows x {w.heads} heads x {w.seq_len} keys "
+        "sample": f"{len(rows)} of {n_rows} query rows x {w.heads} heads x {w.seq_len} keys "
                   f"(fp64 NumPy, {t:.1f} s)",
     }, rows, out, lse
 
@@ -151,16 +158,27 @@ def main():
     dev = torch.device("cuda:0")
     x = W.make_inputs(args.workload)
     w = x["workload"]
-    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    q_key = "q_full" if args.sweep else "q"
+    q, k, v = x[q_key].to(dev), x["k"].to(dev), x["v"].to(dev)
+    n_q = q.shape[1]
     offs = ra.chunk_offsets(w.seq_len, w.n_chunks, w.ring_anything)
-    n_splits, block_m, ws_bytes = ra.forward_plan(tuple(q.shape), offs, args.splits, args.block_m)
-    out = torch.empty((w.batch, w.q_rows, w.heads, w.head_dim), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.batch, w.heads, w.q_rows), dtype=torch.float32, device=dev)
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    out = torch.empty((w.batch, n_q, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.heads, n_q), dtype=torch.float32, device=dev)
+    if args.sweep:
+        # each ring step of each rank is a single-split launch of the library's plan
+        n_splits, block_m, ws_bytes = 1, ra.forward_plan((w.batch, offs[1], w.heads, w.head_dim),
+                                                         [0, offs[1] - offs[0]], 1)[1], 0
+        ws = None
 
-    def step():
-        ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=n_splits, block_m=block_m, out=out,
-                   lse=lse, workspace=ws)
+        def step():
+            ra.ring_sweep(q, k, v, chunk_offsets=offs, scale=x["scale"], out=out, lse=lse)
+    else:
+        n_splits, block_m, ws_bytes = ra.forward_plan(tuple(q.shape), offs, args.splits, args.block_m)
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+
+        def step():
+            ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=n_splits, block_m=block_m,
+                       out=out, lse=lse, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -179,11 +197,11 @@ def main():
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1e3 / args.steps
     avg_ms = float(np.mean(per_launch_ms))
-    flops = float(w.flops)
+    flops = 4.0 * w.batch * n_q * w.seq_len * w.head_dim * w.heads
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
 
-    traffic = traffic_from_profiles(args.workload, block_m)
+    traffic = None if args.sweep else traffic_from_profiles(args.workload, block_m)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -198,10 +216,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": w.name,
-            "description": w.description,
+            "workload": f"{w.name}_ring_sweep" if args.sweep else w.name,
+            "description": (f"every rank of the ring on one GPU ({w.n_chunks} ranks, rank-rotated chunk order, "
+                            f"float32 merge per step); " if args.sweep else "") + w.description,
             "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
-            "q_rows": w.q_rows, "kv_rows": w.seq_len, "n_chunks": w.n_chunks,
+            "q_rows": n_q, "kv_rows": w.seq_len, "n_chunks": w.n_chunks,
             "ring_anything": w.ring_anything,
             "flops_per_step": flops,
             "splits": n_splits,
@@ -220,7 +239,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        cb, rows, ref_out, ref_lse = cpu_baseline(x, args.cpu_seconds)
+        cb, rows, ref_out, ref_lse = cpu_baseline(x, args.cpu_seconds, q_key)
         result["cpu_baseline"] = cb
         o = out[:, rows].detach().cpu().double().numpy()
         l = lse[:, :, rows].detach().cpu().double().numpy()

@@ -16,6 +16,7 @@ from .ringattn import (
     merge,
     new_accumulators,
     ring_shard,
+    ring_sweep,
     step,
 )
 from ._lib import RingAttnError
@@ -31,5 +32,6 @@ __all__ = [
     "merge",
     "new_accumulators",
     "ring_shard",
+    "ring_sweep",
     "step",
 ]

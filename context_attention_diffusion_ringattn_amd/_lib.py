@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "ringattn_merge",
     "ringattn_forward_plan",
     "ringattn_forward",
+    "ringattn_ring_sweep",
 )
 
 
@@ -85,6 +86,7 @@ _SIGNATURES = {
     "ringattn_forward_plan": (ctypes.c_int, [_shape_p, _i64p, _i32, _i64, _plan_p]),
     "ringattn_forward": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _plan_p, _vp,
                                         _sz, _vp]),
+    "ringattn_ring_sweep": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _vp]),
 }
 
 

@@ -20,7 +20,7 @@ using namespace ringattn;
 
 static_assert(kMaxChunks == RINGATTN_MAX_CHUNKS, "chunk limit mismatch");
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 thread_local std::string g_last_error;
 
@@ -224,6 +224,8 @@ void fill_common(AttnArgs *a, const uint16_t *q, const uint16_t *k, const uint16
     a->out = out;
     a->lse = lse;
     a->q_len = s->q_len;
+    a->q_pitch = s->q_len;
+    a->lse_pitch = s->q_len;
     a->batch = s->batch;
     a->heads = s->heads;
     a->scale = scale;
@@ -397,6 +399,62 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     m.split_out_stride = p.split_out_stride;
     m.split_lse_stride = p.split_lse_stride;
     return check_hip(launch_merge_splits(m, shape->head_dim, s), "split merge launch");
+}
+
+int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
+                        int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
+                        const ringattn_shape *shape, void *stream) {
+    int st;
+    if ((st = check_shape(shape, true))) return st;
+    if (shape->kv_len != shape->q_len)
+        return fail(RINGATTN_EINVAL, "ring sweep: q_len %lld must equal kv_len %lld (every rank's rows)",
+                    (long long)shape->q_len, (long long)shape->kv_len);
+    if ((st = check_ptr(q, 16, "q"))) return st;
+    if ((st = check_ptr(k, 16, "k"))) return st;
+    if ((st = check_ptr(v, 16, "v"))) return st;
+    if ((st = check_ptr(out, 16, "out"))) return st;
+    if ((st = check_ptr(lse, 4, "lse"))) return st;
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(RINGATTN_EINVAL, "scale must be finite and > 0");
+    Layout L;  // validates the offsets and the padded stride
+    if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
+
+    const int64_t S = shape->q_len;
+    const int64_t HD = (int64_t)shape->heads * shape->head_dim;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t n_out = (int64_t)shape->batch * S * HD;
+    const int64_t n_lse = (int64_t)shape->batch * shape->heads * S;
+    if ((st = check_hip(launch_acc_init(out, lse, n_out, n_lse, s), "acc_init launch"))) return st;
+
+    for (int r = 0; r < n_chunks; ++r) {
+        const int64_t q0 = chunk_offsets[r], q_len = chunk_offsets[r + 1] - chunk_offsets[r];
+        if (q_len == 0) continue;
+        for (int step = 0; step < n_chunks; ++step) {
+            const int c = (r + step) % n_chunks;
+            const int64_t len = chunk_offsets[c + 1] - chunk_offsets[c];
+            if (len == 0) continue;  // an empty chunk is the merge identity
+            const int64_t row0 = kv_chunk_stride > 0 ? (int64_t)c * kv_chunk_stride : chunk_offsets[c];
+            ringattn_shape rs = *shape;
+            rs.q_len = q_len;
+            rs.kv_len = len;
+            Layout cl;
+            const int64_t offs[2] = {0, len};
+            if ((st = build_layout(offs, 1, 0, len, &cl))) return st;
+            Plan p;
+            if ((st = make_plan(&rs, cl.ct, 1, 0, &p))) return st;
+            AttnArgs a;
+            std::memset(&a, 0, sizeof a);
+            fill_common(&a, q + q0 * HD, k + row0 * HD, v + row0 * HD, out + q0 * HD, lse + q0, scale, &rs);
+            a.q_pitch = S;      // the rank's rows sit inside the full-sequence q / out / lse
+            a.lse_pitch = S;
+            a.ct = cl.ct;
+            a.kv_rows = L.kv_rows;
+            a.n_qtiles = p.n_qtiles;
+            a.n_splits = 1;
+            if ((st = check_hip(launch_plan(a, p, shape->head_dim, kModeAccum, cl.chunked, s), "attention launch")))
+                return st;
+        }
+    }
+    return ok();
 }
 
 }  // extern "C"

@@ -165,7 +165,7 @@ void attn_pp_kernel(const AttnArgs a) {
     // ---- Q operand (registers for the whole sweep) --------------------------
     const int64_t qrow = (int64_t)qt * kPPBlockM + wave * 32 + col;
     const int64_t qrow_ld = qrow < a.q_len ? qrow : a.q_len - 1;
-    const uint16_t *qp = a.q + ((int64_t)b * a.q_len + qrow_ld) * HD + (int64_t)h * D + 8 * half;
+    const uint16_t *qp = a.q + ((int64_t)b * a.q_pitch + qrow_ld) * HD + (int64_t)h * D + 8 * half;
     bf16x8 qreg[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
@@ -430,8 +430,8 @@ void attn_pp_kernel(const AttnArgs a) {
     const bool any_keys = T > 0;
     if (MODE == kModeAccum && !any_keys) return;
 
-    float *orow = a.out + ((int64_t)b * a.q_len + qrow) * HD + (int64_t)h * D + 4 * half;
-    float *lptr = a.lse + ((int64_t)b * a.heads + h) * a.q_len + qrow;
+    float *orow = a.out + ((int64_t)b * a.q_pitch + qrow) * HD + (int64_t)h * D + 4 * half;
+    float *lptr = a.lse + ((int64_t)b * a.heads + h) * a.lse_pitch + qrow;
     if (MODE == kModePartial) {
         orow += (int64_t)split * a.split_out_stride;
         lptr += (int64_t)split * a.split_lse_stride;

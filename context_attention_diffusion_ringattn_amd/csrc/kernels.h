@@ -37,6 +37,8 @@ struct AttnArgs {
     float *out;
     float *lse;
     int64_t q_len;
+    int64_t q_pitch;           // rows per batch in the q and out buffers (>= q_len)
+    int64_t lse_pitch;         // lse entries per (batch, head) (>= q_len)
     int64_t kv_rows;           // rows per batch in the k / v buffers
     int32_t batch;
     int32_t heads;

@@ -243,6 +243,52 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     return out, lse
 
 
+def ring_sweep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+               chunk_offsets: Optional[Sequence[int]] = None,
+               ring_degree: Optional[int] = None,
+               ring_anything: bool = False,
+               kv_chunk_stride: int = 0,
+               scale: Optional[float] = None,
+               out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Every rank of the ring on this GPU (``ringattn_ring_sweep``).
+
+    ``q`` is the full sequence ``[B, S, H, D]`` (rank r's shard is rows
+    ``[offsets[r], offsets[r+1])``); each rank visits the chunks in the order
+    r, r+1, ... (mod N) with a float32 LSE merge after every step.  Returns
+    (out ``[B, S, H, D]`` fp32, lse ``[B, H, S]`` fp32) for all ranks' rows.
+    """
+    _check_bf16(q, "q")
+    _check_bf16(k, "k")
+    _check_bf16(v, "v")
+    B, S, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError(f"k/v shapes {tuple(k.shape)} / {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if chunk_offsets is None:
+        if kv_chunk_stride:
+            raise ValueError("kv_chunk_stride needs explicit chunk_offsets")
+        chunk_offsets = _library_chunk_offsets(S, int(ring_degree or 1), ring_anything)
+    offs = [int(x) for x in chunk_offsets]
+    n_chunks = len(offs) - 1
+    rows_needed = n_chunks * int(kv_chunk_stride) if kv_chunk_stride else offs[-1]
+    if k.shape[1] != rows_needed:
+        raise ValueError(f"k/v hold {k.shape[1]} rows per batch, the chunk layout needs {rows_needed}")
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _check_f32(out, "out", (B, S, H, D), q.device)
+    _check_f32(lse, "lse", (B, H, S), q.device)
+    shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=S, kv_len=offs[-1])
+    check(lib().ringattn_ring_sweep(_ptr(q), _ptr(k), _ptr(v), offsets_array(offs), n_chunks, int(kv_chunk_stride),
+                                    _ptr(out), _ptr(lse), ctypes.c_float(scale), ctypes.byref(shape),
+                                    _stream_handle(q.device, stream)), "ringattn_ring_sweep")
+    return out, lse
+
+
 def ring_shard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, config: RingConfig, *,
                scale: Optional[float] = None, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward for one GPU's share under a ``RingConfig``: ring_degree chunks

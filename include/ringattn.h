@@ -180,6 +180,30 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      float *out, float *lse, float scale, const ringattn_shape *shape,
                      const ringattn_plan *plan, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The whole ring on one GPU: all n_chunks ranks of a ring over a sequence of
+ * S = shape->q_len = shape->kv_len tokens.  Rank r holds query rows
+ * [offsets[r], offsets[r+1]) and K/V chunk r (chunk_offsets as in
+ * ringattn_forward, plain or Ring Anything).  For each rank, the output rows
+ * of its shard start at the merge identity; at ring step s = 0..n_chunks-1
+ * the rank attends to chunk (r + s) mod n_chunks -- the order in which a ring
+ * that passes K/V blocks to the neighbouring rank delivers them -- and merges
+ * that partial into its rows in float32 exactly as ringattn_step does (context
+ * parallelism guide, section "Ring Attention": after one full turn of the
+ * ring every rank has attended to the K/V of every token; Parallelism API
+ * page, ContextParallelConfig.convert_to_fp32).
+ *   q: [B, S, H, D] bf16, every rank's rows;
+ *   k, v: [B, rows, H, D] bf16, packed (kv_chunk_stride = 0, rows = S) or the
+ *     padded Ring Anything buffer (kv_chunk_stride > 0, rows =
+ *     n_chunks * kv_chunk_stride; padding rows are never read);
+ *   out: [B, S, H, D] float32, lse: [B, H, S] float32, fully written.
+ * Enqueues one initialisation and at most n_chunks^2 attention launches on
+ * `stream` (none for empty ranks or chunks).  scale must be finite and > 0.
+ */
+int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const int64_t *chunk_offsets, int32_t n_chunks, int64_t kv_chunk_stride,
+                        float *out, float *lse, float scale, const ringattn_shape *shape, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

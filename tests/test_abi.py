@@ -40,7 +40,7 @@ def test_header_symbols_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ringattn_abi_version() == 2
+    assert L.ringattn_abi_version() == 3
     assert _lib.status_string(0) == "RINGATTN_OK"
     assert _lib.status_string(-1) == "RINGATTN_EINVAL"
     assert _lib.status_string(-2) == "RINGATTN_EUNSUPPORTED"
@@ -158,6 +158,28 @@ def test_forward_offset_errors(L):
     assert _fwd(L, [0, 128, 256], s, scale=0.0) == _lib.RINGATTN_EINVAL
     assert _fwd(L, [0, 128, 256], s, scale=-0.125) == _lib.RINGATTN_EINVAL
     assert _fwd(L, [0, 128, 256], shape(D=80)) == _lib.RINGATTN_EUNSUPPORTED
+
+
+def _sweep(L, offs, s, stride=0, q=P, out=P, lse=P, scale=0.125):
+    arr = _lib.offsets_array(offs) if offs is not None else None
+    return L.ringattn_ring_sweep(q, P, P, arr, len(offs) - 1 if offs else 0, stride, out, lse, scale,
+                                 ctypes.byref(s), None)
+
+
+def test_ring_sweep_errors(L):
+    """The sweep validates like ringattn_forward, and needs q_len == kv_len
+    (q holds every rank's rows)."""
+    s = shape(Sq=256, Skv=256)
+    assert _sweep(L, None, s) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 128, 256], shape(Sq=128, Skv=256)) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [1, 128, 256], s) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 128, 255], s) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 200, 100, 256], s) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 128, 256], s, stride=100) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 128, 256], s, out=P_MISALIGNED) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 128, 256], s, q=None) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 128, 256], s, scale=0.0) == _lib.RINGATTN_EINVAL
+    assert _sweep(L, [0, 128, 256], shape(D=80, Sq=256, Skv=256)) == _lib.RINGATTN_EUNSUPPORTED
 
 
 def test_forward_workspace_error(L):
