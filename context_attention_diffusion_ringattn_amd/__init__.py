@@ -10,6 +10,7 @@ from .ringattn import (
     RingConfig,
     acc_init,
     chunk_offsets,
+    cp_share,
     default_scale,
     forward,
     forward_plan,
@@ -26,6 +27,7 @@ __all__ = [
     "RingAttnError",
     "acc_init",
     "chunk_offsets",
+    "cp_share",
     "default_scale",
     "forward",
     "forward_plan",

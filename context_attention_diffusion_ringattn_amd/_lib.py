@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "ringattn_forward_plan",
     "ringattn_forward",
     "ringattn_ring_sweep",
+    "ringattn_cp_layout",
 )
 
 
@@ -51,6 +52,31 @@ class Plan(ctypes.Structure):
         ("n_splits", ctypes.c_int32),
         ("block_m", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
+class CpConfig(ctypes.Structure):
+    _fields_ = [
+        ("seq_len", ctypes.c_int64),
+        ("heads", ctypes.c_int32),
+        ("ring_degree", ctypes.c_int32),
+        ("ulysses_degree", ctypes.c_int32),
+        ("ring_anything", ctypes.c_int32),
+        ("ulysses_anything", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class CpShare(ctypes.Structure):
+    _fields_ = [
+        ("ring_index", ctypes.c_int32),
+        ("ulysses_index", ctypes.c_int32),
+        ("token_begin", ctypes.c_int64),
+        ("token_end", ctypes.c_int64),
+        ("q_begin", ctypes.c_int64),
+        ("q_end", ctypes.c_int64),
+        ("head_begin", ctypes.c_int32),
+        ("head_end", ctypes.c_int32),
     ]
 
 
@@ -87,6 +113,7 @@ _SIGNATURES = {
     "ringattn_forward": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _plan_p, _vp,
                                         _sz, _vp]),
     "ringattn_ring_sweep": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _vp]),
+    "ringattn_cp_layout": (ctypes.c_int, [ctypes.POINTER(CpConfig), _i32, ctypes.POINTER(CpShare)]),
 }
 
 

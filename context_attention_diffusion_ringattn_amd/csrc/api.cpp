@@ -20,7 +20,7 @@ using namespace ringattn;
 
 static_assert(kMaxChunks == RINGATTN_MAX_CHUNKS, "chunk limit mismatch");
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 
 thread_local std::string g_last_error;
 
@@ -454,6 +454,50 @@ int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 return st;
         }
     }
+    return ok();
+}
+
+// Piece i of n of a length-`len` range, the first len % n pieces one longer.
+static void even_piece(int64_t len, int64_t n, int64_t i, int64_t *begin, int64_t *end) {
+    const int64_t base = len / n, rem = len % n;
+    *begin = i * base + (i < rem ? i : rem);
+    *end = *begin + base + (i < rem ? 1 : 0);
+}
+
+int ringattn_cp_layout(const ringattn_cp_config *cfg, int32_t rank, ringattn_cp_share *share) {
+    if (!cfg) return fail(RINGATTN_EINVAL, "config is NULL");
+    if (!share) return fail(RINGATTN_EINVAL, "share is NULL");
+    if (cfg->reserved != 0) return fail(RINGATTN_EINVAL, "config.reserved must be 0");
+    const int64_t S = cfg->seq_len;
+    const int32_t H = cfg->heads, R = cfg->ring_degree, U = cfg->ulysses_degree;
+    if (S < 0) return fail(RINGATTN_EINVAL, "seq_len must be >= 0");
+    if (H < 1) return fail(RINGATTN_EINVAL, "heads must be >= 1");
+    if (R < 1 || R > kMaxChunks) return fail(RINGATTN_EINVAL, "ring_degree %d outside [1, %d]", R, kMaxChunks);
+    if (U < 1 || U > (1 << 20)) return fail(RINGATTN_EINVAL, "ulysses_degree %d outside [1, 2^20]", U);
+    const bool ra = cfg->ring_anything != 0, ua = cfg->ulysses_anything != 0;
+    if (ra && ua) return fail(RINGATTN_EINVAL, "ring_anything and ulysses_anything do not combine");
+    if (ra && !(R > 1 && U == 1)) return fail(RINGATTN_EINVAL, "ring_anything needs ring_degree > 1 and ulysses_degree 1");
+    if (ua && !(U > 1 && R == 1)) return fail(RINGATTN_EINVAL, "ulysses_anything needs ulysses_degree > 1 and ring_degree 1");
+    const int64_t world = (int64_t)R * U;
+    if (rank < 0 || rank >= world) return fail(RINGATTN_EINVAL, "rank %d outside [0, %lld)", rank, (long long)world);
+    if (!ra && !ua) {
+        if (S % world != 0)
+            return fail(RINGATTN_EINVAL, "seq_len %lld does not divide by ring_degree * ulysses_degree = %lld",
+                        (long long)S, (long long)world);
+        if (H % U != 0) return fail(RINGATTN_EINVAL, "heads %d do not divide by ulysses_degree %d", H, U);
+    }
+    ringattn_cp_share sh;
+    sh.ring_index = rank / U;
+    sh.ulysses_index = rank % U;
+    // the sequence before the all-to-all: R*U pieces in rank order
+    even_piece(S, world, rank, &sh.token_begin, &sh.token_end);
+    // query rows of the share: ring chunk r
+    even_piece(S, R, sh.ring_index, &sh.q_begin, &sh.q_end);
+    int64_t h0, h1;
+    even_piece(H, U, sh.ulysses_index, &h0, &h1);
+    sh.head_begin = (int32_t)h0;
+    sh.head_end = (int32_t)h1;
+    *share = sh;
     return ok();
 }
 

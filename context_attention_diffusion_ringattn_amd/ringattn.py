@@ -289,6 +289,21 @@ def ring_sweep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     return out, lse
 
 
+def cp_share(seq_len: int, heads: int, *, ring_degree: int = 1, ulysses_degree: int = 1,
+             ring_anything: bool = False, ulysses_anything: bool = False, rank: int = 0) -> dict:
+    """Layout of `rank` in the ring x Ulysses grid (``ringattn_cp_layout``):
+    ``ring_index``, ``ulysses_index``, its tokens before the Ulysses
+    all-to-all (``token_begin``/``token_end``) and the query rows
+    (``q_begin``/``q_end``) and heads (``head_begin``/``head_end``) of its
+    attention share, which attends to the ring chunks of the same heads."""
+    cfg = _lib.CpConfig(seq_len=int(seq_len), heads=int(heads), ring_degree=int(ring_degree),
+                        ulysses_degree=int(ulysses_degree), ring_anything=int(bool(ring_anything)),
+                        ulysses_anything=int(bool(ulysses_anything)), reserved=0)
+    out = _lib.CpShare()
+    check(lib().ringattn_cp_layout(ctypes.byref(cfg), int(rank), ctypes.byref(out)), "ringattn_cp_layout")
+    return {k: getattr(out, k) for k, _ in _lib.CpShare._fields_}
+
+
 def ring_shard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, config: RingConfig, *,
                scale: Optional[float] = None, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward for one GPU's share under a ``RingConfig``: ring_degree chunks

@@ -82,6 +82,18 @@ WORKLOADS: Dict[str, Workload] = {
         description="Video-scale ring shard: B=1 H=24 D=128 S=65536 (16 frames x 64x64 tokens), "
                     "ring degree 8, local Q 8192 rows vs 8 K/V chunks of 8192, bf16 N(0,1) "
                     "with 0.5% Q/K outlier rows x6"),
+    "usp": Workload(
+        "usp", batch=1, heads=12, head_dim=128, seq_len=65536, n_chunks=4, ring_anything=False,
+        q_rows=16384, seed=5,
+        description="Unified (Ulysses 2 x ring 4, 8 GPUs) share of the video sequence: rank (r=0, u=0) "
+                    "holds query rows 0..16383 (ring chunk 0) of heads 0..11 after the all-to-all and "
+                    "attends to 4 K/V chunks of 16384, B=1 D=128, bf16 N(0,1)"),
+    "ulysses_anything": Workload(
+        "ulysses_anything", batch=1, heads=6, head_dim=128, seq_len=4481, n_chunks=1, ring_anything=False,
+        q_rows=4481, seed=6,
+        description="Ulysses Anything share of FLUX at 1008x1008 on 4 GPUs: S=4481 (3969 image + 512 text "
+                    "tokens, not divisible by 4), 24 heads / 4 = 6 heads per GPU, one full non-causal "
+                    "pass, B=1 D=128, bf16 N(0,1)"),
 }
 
 

@@ -204,6 +204,56 @@ int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         const int64_t *chunk_offsets, int32_t n_chunks, int64_t kv_chunk_stride,
                         float *out, float *lse, float scale, const ringattn_shape *shape, void *stream);
 
+/*
+ * Context-parallel layout of one rank: which tokens it holds, and which query
+ * rows and heads make up its attention share, for plain ring, Ring Anything,
+ * Ulysses, Ulysses Anything and Unified (ring x Ulysses) attention.
+ *
+ * The GPUs form a 2D grid of ring_degree x ulysses_degree; rank = r * U + u
+ * with r the ring index and u the Ulysses index (a mesh whose dims are
+ * ("ring", "ulysses"), row-major).  Every rank is in one Ulysses group (same
+ * r) and one ring group (same u) (context parallelism guide, section
+ * "Perhatian Terpadu"; Parallelism API page, ContextParallelConfig.mesh).
+ *   token_begin/end: the rank's slice of the sequence before the Ulysses
+ *     all-to-all: the sequence split into R*U pieces in rank order (R pieces
+ *     for Ring Anything, U for Ulysses Anything), all heads;
+ *   q_begin/end: its query rows after the all-to-all: ring chunk r, the union
+ *     of the pieces of its Ulysses group (all S rows when R == 1);
+ *   head_begin/end: its head block: block u of the H heads.
+ * The share is: q rows [q_begin, q_end) and heads [head_begin, head_end)
+ * attend to every token of the ring chunks (offsets from
+ * ringattn_chunk_offsets(seq_len, R, ring_anything)) of the same heads.
+ * Rules (guide, variant table and sections "Ulysses Anything Attention",
+ * "Ring Anything Attention"; API page, ulysses_anything / ring_anything):
+ *   plain: seq_len must divide by R * U and heads by U;
+ *   ring_anything: R > 1 and U == 1, any seq_len; the first S mod R chunks
+ *     hold one extra token;
+ *   ulysses_anything: U > 1 and R == 1, any seq_len and head count; the first
+ *     S mod U pieces hold one extra token and the first H mod U blocks one
+ *     extra head (a block may be empty when H < U);
+ *   the two "anything" modes do not combine; R <= RINGATTN_MAX_CHUNKS.
+ * Violations give RINGATTN_EINVAL.  Pure host code.
+ */
+typedef struct ringattn_cp_config {
+    int64_t seq_len;          /* S >= 0 tokens of the whole sequence */
+    int32_t heads;            /* H >= 1 attention heads of the layer */
+    int32_t ring_degree;      /* R >= 1 */
+    int32_t ulysses_degree;   /* U >= 1 */
+    int32_t ring_anything;    /* nonzero: Ring Anything */
+    int32_t ulysses_anything; /* nonzero: Ulysses Anything */
+    int32_t reserved;         /* must be 0 */
+} ringattn_cp_config;
+
+typedef struct ringattn_cp_share {
+    int32_t ring_index;       /* r = rank / U */
+    int32_t ulysses_index;    /* u = rank % U */
+    int64_t token_begin, token_end;
+    int64_t q_begin, q_end;
+    int32_t head_begin, head_end;
+} ringattn_cp_share;
+
+int ringattn_cp_layout(const ringattn_cp_config *config, int32_t rank, ringattn_cp_share *share);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,11 @@ What it computes, and where that is defined:
   ``math.fsum`` for tiny shapes.
 * ``ulysses_head_range`` -- the head subset one GPU holds after the Ulysses
   all-to-all (guide, section "Perhatian Ulysses").
+* ``cp_share`` / ``cp_mesh`` -- one rank's layout in the ring x Ulysses grid
+  (Unified attention, Ulysses Anything, Ring Anything): its tokens before the
+  all-to-all and the query rows and heads of its attention share (guide,
+  sections "Perhatian Terpadu", "Ulysses Anything Attention"; API page,
+  ``ContextParallelConfig``).
 
 Every function here is pinned by a test in ``tests/test_oracle.py`` to
 something other than itself (closed forms, a library routine, brute force,
@@ -33,6 +38,7 @@ invariants).  No function is parity unpinned.
 """
 
 from .offsets import chunk_offsets, chunk_lengths, padded_chunk_length, pad_gather_slice
+from .partition import cp_mesh, cp_share
 from .attention import (
     attention_fp64,
     attention_rows_fp64,
@@ -55,4 +61,6 @@ __all__ = [
     "ring_shard_fp64",
     "ulysses_head_range",
     "brute_force_attention",
+    "cp_mesh",
+    "cp_share",
 ]
