@@ -16,9 +16,11 @@ from .ringattn import (
     forward_plan,
     merge,
     new_accumulators,
+    new_accumulators_bf16,
     ring_shard,
     ring_sweep,
     step,
+    step_bf16,
 )
 from ._lib import RingAttnError
 
@@ -33,7 +35,9 @@ __all__ = [
     "forward_plan",
     "merge",
     "new_accumulators",
+    "new_accumulators_bf16",
     "ring_shard",
     "ring_sweep",
     "step",
+    "step_bf16",
 ]

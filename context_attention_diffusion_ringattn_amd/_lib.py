@@ -33,6 +33,8 @@ EXPORTED_SYMBOLS = (
     "ringattn_forward",
     "ringattn_ring_sweep",
     "ringattn_cp_layout",
+    "ringattn_acc_init_bf16",
+    "ringattn_step_bf16",
 )
 
 
@@ -114,6 +116,8 @@ _SIGNATURES = {
                                         _sz, _vp]),
     "ringattn_ring_sweep": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _vp]),
     "ringattn_cp_layout": (ctypes.c_int, [ctypes.POINTER(CpConfig), _i32, ctypes.POINTER(CpShare)]),
+    "ringattn_acc_init_bf16": (ctypes.c_int, [_vp, _vp, _shape_p, _vp]),
+    "ringattn_step_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _shape_p, _vp]),
 }
 
 

@@ -20,7 +20,7 @@ using namespace ringattn;
 
 static_assert(kMaxChunks == RINGATTN_MAX_CHUNKS, "chunk limit mismatch");
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 
 thread_local std::string g_last_error;
 
@@ -499,6 +499,44 @@ int ringattn_cp_layout(const ringattn_cp_config *cfg, int32_t rank, ringattn_cp_
     sh.head_end = (int32_t)h1;
     *share = sh;
     return ok();
+}
+
+int ringattn_acc_init_bf16(uint16_t *out_acc, uint16_t *lse_acc, const ringattn_shape *shape, void *stream) {
+    int st;
+    if ((st = check_shape(shape, false))) return st;
+    if ((st = check_ptr(out_acc, 8, "out_acc"))) return st;
+    if ((st = check_ptr(lse_acc, 2, "lse_acc"))) return st;
+    const int64_t n_out = (int64_t)shape->batch * shape->q_len * shape->heads * shape->head_dim;
+    const int64_t n_lse = (int64_t)shape->batch * shape->heads * shape->q_len;
+    return check_hip(launch_acc_init_bf16(out_acc, lse_acc, n_out, n_lse, (hipStream_t)stream), "acc_init launch");
+}
+
+int ringattn_step_bf16(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk, uint16_t *out_acc,
+                       uint16_t *lse_acc, float scale, const ringattn_shape *shape, void *stream) {
+    int st;
+    if ((st = check_shape(shape, true))) return st;
+    if ((st = check_ptr(q, 16, "q"))) return st;
+    if ((st = check_ptr(out_acc, 8, "out_acc"))) return st;
+    if ((st = check_ptr(lse_acc, 2, "lse_acc"))) return st;
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(RINGATTN_EINVAL, "scale must be finite and > 0");
+    if (shape->kv_len == 0) return ok();
+    if ((st = check_ptr(k_chunk, 16, "k_chunk"))) return st;
+    if ((st = check_ptr(v_chunk, 16, "v_chunk"))) return st;
+    Layout L;
+    const int64_t offs[2] = {0, shape->kv_len};
+    if ((st = build_layout(offs, 1, 0, shape->kv_len, &L))) return st;
+    Plan p;
+    if ((st = make_plan(shape, L.ct, 1, 256, &p))) return st;  // the 8-wave kernel has the bf16 epilogue
+    AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    fill_common(&a, q, k_chunk, v_chunk, reinterpret_cast<float *>(out_acc), reinterpret_cast<float *>(lse_acc),
+                scale, shape);
+    a.ct = L.ct;
+    a.kv_rows = L.kv_rows;
+    a.n_qtiles = p.n_qtiles;
+    a.n_splits = 1;
+    return check_hip(launch_plan(a, p, shape->head_dim, kModeAccumBf16, L.chunked, (hipStream_t)stream),
+                     "attention launch");
 }
 
 }  // extern "C"

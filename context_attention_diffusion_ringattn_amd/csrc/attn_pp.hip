@@ -428,7 +428,7 @@ void attn_pp_kernel(const AttnArgs a) {
     const float l_tot = l_lane + other_half(l_lane, half != 0);
     if (qrow >= a.q_len) return;
     const bool any_keys = T > 0;
-    if (MODE == kModeAccum && !any_keys) return;
+    if ((MODE == kModeAccum || MODE == kModeAccumBf16) && !any_keys) return;
 
     float *orow = a.out + ((int64_t)b * a.q_pitch + qrow) * HD + (int64_t)h * D + 4 * half;
     float *lptr = a.lse + ((int64_t)b * a.heads + h) * a.lse_pitch + qrow;
@@ -439,7 +439,49 @@ void attn_pp_kernel(const AttnArgs a) {
     const float inv_l = any_keys ? 1.f / l_tot : 0.f;
     const float lse_chunk = any_keys ? fmaf(m_run, a.scale, logf(l_tot)) : -INFINITY;
 
-    if (MODE == kModeAccum) {
+    if (MODE == kModeAccumBf16) {
+        // Accumulators kept in bf16 between steps: the partial is rounded to
+        // bf16 (as a bf16-output attention pass returns it), merged in
+        // float32 with the stored state, and the result rounded back.
+        uint16_t *o16 = (uint16_t *)a.out + ((int64_t)b * a.q_pitch + qrow) * HD + (int64_t)h * D + 4 * half;
+        uint16_t *l16 = (uint16_t *)a.lse + ((int64_t)b * a.heads + h) * a.lse_pitch + qrow;
+        const float lc = (float)(__bf16)lse_chunk;
+        const float la = (float)__builtin_bit_cast(__bf16, *l16);
+        float wa, wb, lse_new;
+        if (la == -INFINITY) {
+            wa = 0.f;
+            wb = 1.f;
+            lse_new = lc;
+        } else {
+            lse_new = fmaxf(la, lc) + log1pf(expf(-fabsf(la - lc)));
+            wa = expf(la - lse_new);
+            wb = expf(lc - lse_new);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint16_t *p = o16 + 32 * db + 8 * g;
+                const uint2 cur = *(const uint2 *)p;
+                float r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float part = (float)(__bf16)(o[db][4 * g + e] * inv_l);
+                    const uint32_t word = e < 2 ? cur.x : cur.y;
+                    const uint16_t bits = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+                    const float acc = (float)__builtin_bit_cast(__bf16, bits);
+                    r[e] = la == -INFINITY ? part : fmaf(wa, acc, wb * part);
+                }
+                uint2 res;
+                res.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[1]) << 16);
+                res.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[2]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[3]) << 16);
+                *(uint2 *)p = res;
+            }
+        }
+        if (half == 0) *l16 = __builtin_bit_cast(uint16_t, (__bf16)lse_new);
+    } else if (MODE == kModeAccum) {
         const float la = *lptr;
         float wa, wb, lse_new;
         if (la == -INFINITY) {
@@ -492,6 +534,10 @@ hipError_t launch_pp_dc(const AttnArgs &a, EpilogueMode mode, hipStream_t stream
         case kModeAccum:
             hipLaunchKernelGGL((attn_pp_kernel<D, kModeAccum, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads), 0,
                                stream, a);
+            break;
+        case kModeAccumBf16:
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModeAccumBf16, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads),
+                               0, stream, a);
             break;
     }
     return hipGetLastError();

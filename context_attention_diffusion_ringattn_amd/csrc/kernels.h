@@ -28,6 +28,7 @@ enum EpilogueMode : int32_t {
     kModeFinal = 0,    // write normalised out and lse
     kModePartial = 1,  // write normalised out and lse of this split into its workspace slot
     kModeAccum = 2,    // LSE-merge into out/lse in place (ring step)
+    kModeAccumBf16 = 3,  // the same with bf16 out/lse accumulators (out/lse point to uint16_t)
 };
 
 struct AttnArgs {
@@ -71,5 +72,6 @@ hipError_t launch_merge_splits(const MergeSplitsArgs &a, int head_dim, hipStream
 hipError_t launch_merge2(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
                          int64_t q_len, int32_t batch, int32_t heads, int32_t head_dim, hipStream_t stream);
 hipError_t launch_acc_init(float *out, float *lse, int64_t n_out, int64_t n_lse, hipStream_t stream);
+hipError_t launch_acc_init_bf16(uint16_t *out, uint16_t *lse, int64_t n_out, int64_t n_lse, hipStream_t stream);
 
 }  // namespace ringattn

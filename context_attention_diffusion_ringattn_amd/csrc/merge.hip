@@ -103,6 +103,13 @@ __global__ __launch_bounds__(kMergeThreads) void acc_init_kernel(float *out, flo
     if (gid < n_lse) lse[gid] = -INFINITY;
 }
 
+__global__ __launch_bounds__(kMergeThreads) void acc_init_bf16_kernel(uint16_t *out, uint16_t *lse, int64_t n_out4,
+                                                                     int64_t n_lse) {
+    const int64_t gid = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    if (gid < n_out4) ((uint2 *)out)[gid] = uint2{0u, 0u};
+    if (gid < n_lse) lse[gid] = 0xff80u;  // bf16 -inf
+}
+
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kMergeThreads - 1) / kMergeThreads); }
 
 }  // namespace
@@ -133,6 +140,14 @@ hipError_t launch_acc_init(float *out, float *lse, int64_t n_out, int64_t n_lse,
     const int64_t n = n4 > n_lse ? n4 : n_lse;
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(acc_init_kernel, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, out, lse, n4, n_lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_acc_init_bf16(uint16_t *out, uint16_t *lse, int64_t n_out, int64_t n_lse, hipStream_t stream) {
+    const int64_t n4 = n_out / 4;
+    const int64_t n = n4 > n_lse ? n4 : n_lse;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(acc_init_bf16_kernel, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, out, lse, n4, n_lse);
     return hipGetLastError();
 }
 

@@ -152,6 +152,39 @@ def step(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out_acc:
           "ringattn_step")
 
 
+def new_accumulators_bf16(q: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 accumulators for q (the convert_to_fp32=False mode) set to the
+    empty state by ``ringattn_acc_init_bf16``."""
+    B, Sq, H, D = q.shape
+    out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.bfloat16, device=q.device)
+    shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=0)
+    check(lib().ringattn_acc_init_bf16(_ptr(out), _ptr(lse), ctypes.byref(shape), _stream_handle(q.device, stream)),
+          "ringattn_acc_init_bf16")
+    return out, lse
+
+
+def step_bf16(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out_acc: torch.Tensor,
+              lse_acc: torch.Tensor, scale: Optional[float] = None, stream=None) -> None:
+    """One ring step with bf16 accumulators (``ringattn_step_bf16``): the
+    partial is rounded to bf16, merged, and the state stored as bf16."""
+    _check_bf16(q, "q")
+    _check_bf16(k_chunk, "k_chunk")
+    _check_bf16(v_chunk, "v_chunk")
+    B, Sq, H, D = q.shape
+    if k_chunk.shape != v_chunk.shape or k_chunk.shape[0] != B or k_chunk.shape[2:] != q.shape[2:]:
+        raise ValueError(f"k/v chunk shapes {tuple(k_chunk.shape)} / {tuple(v_chunk.shape)} do not match q")
+    for t, name, shp in ((out_acc, "out_acc", (B, Sq, H, D)), (lse_acc, "lse_acc", (B, H, Sq))):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shp or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shp} on {q.device}")
+    if scale is None:
+        scale = default_scale(D)
+    shape = _shape(q, k_chunk.shape[1])
+    check(lib().ringattn_step_bf16(_ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(out_acc), _ptr(lse_acc),
+                                   ctypes.c_float(scale), ctypes.byref(shape), _stream_handle(q.device, stream)),
+          "ringattn_step_bf16")
+
+
 def merge(out_acc: torch.Tensor, lse_acc: torch.Tensor, out_part: torch.Tensor, lse_part: torch.Tensor,
           stream=None) -> None:
     """LSE-merge a float32 partial into the accumulators in place."""

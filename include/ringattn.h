@@ -254,6 +254,24 @@ typedef struct ringattn_cp_share {
 
 int ringattn_cp_layout(const ringattn_cp_config *config, int32_t rank, ringattn_cp_share *share);
 
+/*
+ * The ring step with bf16 accumulators, the mode ContextParallelConfig's
+ * convert_to_fp32 = False selects (Parallelism API page: without it the
+ * output and LSE are not converted to float32 for the merge).  Built to
+ * measure the error the float32 merge avoids; ringattn_step is the path.
+ *   out_acc: [B, q_len, H, D] bf16, lse_acc: [B, H, q_len] bf16 (uint16_t
+ *   bit patterns, 8- and 2-byte aligned).  ringattn_acc_init_bf16 sets
+ *   out = 0, lse = -inf.  ringattn_step_bf16 computes the chunk partial as
+ *   ringattn_step does, rounds its output and LSE to bf16 (round to nearest
+ *   even), merges them with the stored state by the same formula in float32
+ *   and stores the result rounded to bf16.  Same argument rules as
+ *   ringattn_step; kv_len = 0 is a no-op.
+ */
+int ringattn_acc_init_bf16(uint16_t *out_acc, uint16_t *lse_acc, const ringattn_shape *shape, void *stream);
+int ringattn_step_bf16(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk,
+                       uint16_t *out_acc, uint16_t *lse_acc, float scale,
+                       const ringattn_shape *shape, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,9 @@ What it computes, and where that is defined:
   ``ContextParallelConfig.convert_to_fp32`` keeps in float32 on the GPU.  The
   pages give the purpose of the merge but do not print its formula; the
   oracle uses the exact LSE-weighted combination (see ``lse_merge_fp64``).
+* ``ring_shard_bf16_state_fp64`` -- the ring with its merge state kept in
+  bf16 (``convert_to_fp32 = False``), to measure the error the float32
+  merge avoids.
 * ``brute_force_attention`` -- the same definition in pure-Python loops with
   ``math.fsum`` for tiny shapes.
 * ``ulysses_head_range`` -- the head subset one GPU holds after the Ulysses
@@ -45,6 +48,7 @@ from .attention import (
     chunk_partial_fp64,
     lse_merge_fp64,
     ring_shard_fp64,
+    ring_shard_bf16_state_fp64,
     ulysses_head_range,
 )
 from .brute import brute_force_attention
@@ -59,6 +63,7 @@ __all__ = [
     "chunk_partial_fp64",
     "lse_merge_fp64",
     "ring_shard_fp64",
+    "ring_shard_bf16_state_fp64",
     "ulysses_head_range",
     "brute_force_attention",
     "cp_mesh",

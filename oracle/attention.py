@@ -170,3 +170,37 @@ def ulysses_head_range(n_heads: int, ulysses_degree: int, rank: int) -> Tuple[in
         raise ValueError(f"{n_heads} heads do not divide by ulysses_degree {ulysses_degree}")
     per = n_heads // ulysses_degree
     return rank * per, (rank + 1) * per
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even) and return
+    them as float64; -inf stays -inf."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def ring_shard_bf16_state_fp64(q, k, v, offsets: Sequence[int], scale: float,
+                               order: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """The ring's way with the merge state kept in bf16 -- the mode that
+    ContextParallelConfig.convert_to_fp32 = False selects (Parallelism API
+    page: without it the output and LSE are not converted to float32 for the
+    merge).  Each chunk partial (output, LSE) is rounded to bf16, merged with
+    the stored state by the LSE formula in float64, and the merged state is
+    rounded to bf16 again.  Only used to measure the error that the float32
+    merge avoids."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    n = len(offsets) - 1
+    if order is None:
+        order = range(n)
+    B, Sq, H, D = q.shape
+    out = np.zeros((B, Sq, H, D))
+    lse = np.full((B, H, Sq), -np.inf)
+    for c in order:
+        lo, hi = offsets[c], offsets[c + 1]
+        part_out, part_lse = chunk_partial_fp64(q, k[:, lo:hi], v[:, lo:hi], scale)
+        part_out, part_lse = _round_bf16(part_out), _round_bf16(part_lse)
+        out, lse = lse_merge_fp64(out, lse, part_out, part_lse)
+        out, lse = _round_bf16(out), _round_bf16(lse)
+    return out, lse

@@ -40,7 +40,7 @@ def test_header_symbols_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ringattn_abi_version() == 4
+    assert L.ringattn_abi_version() == 5
     assert _lib.status_string(0) == "RINGATTN_OK"
     assert _lib.status_string(-1) == "RINGATTN_EINVAL"
     assert _lib.status_string(-2) == "RINGATTN_EUNSUPPORTED"
