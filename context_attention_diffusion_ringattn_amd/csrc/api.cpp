@@ -91,10 +91,38 @@ int cu_count_for_current_device() {
 
 // The K/V layout of one call, as the kernels walk it.
 struct Layout {
-    ChunkTable ct;
+    ChunkTable ct;    // 64-key tiles (the 8-wave kernel)
+    ChunkTable ct32;  // 32-key tiles (the 4-wave kernel)
     int64_t kv_rows;  // rows per batch in the k / v buffers
     bool chunked;     // tiles follow the chunk table (padded layout)
 };
+
+// The tile walk of one tile size over validated chunks.
+int fill_table(const int64_t *offsets, int32_t n_chunks, int64_t stride, int64_t kv_len, bool chunked, int tile_n,
+               ChunkTable *ct) {
+    std::memset(ct, 0, sizeof *ct);
+    if (!chunked) {
+        ct->n_chunks = 1;
+        ct->row_start[0] = 0;
+        ct->len[0] = (int32_t)kv_len;
+        ct->tile_start[0] = 0;
+        ct->tile_start[1] = ct->n_tiles = (int32_t)((kv_len + tile_n - 1) / tile_n);
+        return RINGATTN_OK;
+    }
+    ct->n_chunks = n_chunks;
+    int64_t tiles = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t len = offsets[c + 1] - offsets[c];
+        ct->row_start[c] = stride > 0 ? (int64_t)c * stride : offsets[c];
+        ct->len[c] = (int32_t)len;
+        ct->tile_start[c] = (int32_t)tiles;
+        tiles += (len + tile_n - 1) / tile_n;
+        if (tiles > (int64_t)INT32_MAX) return fail(RINGATTN_EINVAL, "too many K/V tiles");
+    }
+    ct->tile_start[n_chunks] = (int32_t)tiles;
+    ct->n_tiles = (int32_t)tiles;
+    return RINGATTN_OK;
+}
 
 // Validate host offsets and build the tile walk.  Packed chunks are one
 // contiguous key range, so they become a single table entry and tiles may
@@ -116,31 +144,11 @@ int build_layout(const int64_t *offsets, int32_t n_chunks, int64_t stride, int64
                         (long long)stride);
         if (len > (int64_t)INT32_MAX - kBlockN) return fail(RINGATTN_EINVAL, "chunk %d too long", c);
     }
-    ChunkTable *ct = &L->ct;
-    std::memset(ct, 0, sizeof *ct);
     L->chunked = stride > 0 || kv_len > (int64_t)INT32_MAX - kBlockN;
     L->kv_rows = stride > 0 ? (int64_t)n_chunks * stride : kv_len;
-    if (!L->chunked) {
-        ct->n_chunks = 1;
-        ct->row_start[0] = 0;
-        ct->len[0] = (int32_t)kv_len;
-        ct->tile_start[0] = 0;
-        ct->tile_start[1] = ct->n_tiles = (int32_t)((kv_len + kBlockN - 1) / kBlockN);
-        return RINGATTN_OK;
-    }
-    ct->n_chunks = n_chunks;
-    int64_t tiles = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-        const int64_t len = offsets[c + 1] - offsets[c];
-        ct->row_start[c] = stride > 0 ? (int64_t)c * stride : offsets[c];
-        ct->len[c] = (int32_t)len;
-        ct->tile_start[c] = (int32_t)tiles;
-        tiles += (len + kBlockN - 1) / kBlockN;
-        if (tiles > (int64_t)INT32_MAX) return fail(RINGATTN_EINVAL, "too many K/V tiles");
-    }
-    ct->tile_start[n_chunks] = (int32_t)tiles;
-    ct->n_tiles = (int32_t)tiles;
-    return RINGATTN_OK;
+    int st;
+    if ((st = fill_table(offsets, n_chunks, stride, kv_len, L->chunked, kBlockN, &L->ct))) return st;
+    return fill_table(offsets, n_chunks, stride, kv_len, L->chunked, 32, &L->ct32);
 }
 
 struct Plan {
@@ -153,15 +161,16 @@ struct Plan {
 };
 
 // Cost model of one launch, in microseconds.  Workgroups run in rounds of
-// `slots` (two 4-wave workgroups or one 8-wave workgroup per CU); a
+// `slots` (one 8-wave workgroup or three 4-wave workgroups per CU); a
 // workgroup costs its tile count times the time one tile takes when every
-// CU is busy, plus a fixed start/finish cost; K/V splits add the float32
+// CU is busy (64-key tiles for the 8-wave kernel, 32-key tiles for the
+// 4-wave one), plus a fixed start/finish cost; K/V splits add the float32
 // partial traffic (written once, read once by the merge) at HBM speed.  The
-// constants are measured-order estimates for MI355X.
+// constants are measured on MI355X (video-sized shards).
 double plan_cost(const ringattn_shape *s, int32_t n_tiles, int block_m, int splits) {
     const double cus = cu_count_for_current_device();
-    const double slots = block_m == 256 ? cus : 2.0 * cus;
-    const double tile_us = block_m == 256 ? 1.45 : 2.2;  // one 64-key tile of one workgroup
+    const double slots = block_m == 256 ? cus : 3.0 * cus;
+    const double tile_us = block_m == 256 ? 1.79 : 1.47;
     const double fixed_us = 3.0;
     const double n_qtiles = std::ceil((double)s->q_len / block_m);
     const double base = n_qtiles * s->heads * s->batch;
@@ -175,20 +184,21 @@ double plan_cost(const ringattn_shape *s, int32_t n_tiles, int block_m, int spli
     return cost;
 }
 
-int make_plan(const ringattn_shape *s, const ChunkTable &ct, int32_t req_splits, int32_t req_block_m, Plan *p) {
+int make_plan(const ringattn_shape *s, const Layout &L, int32_t req_splits, int32_t req_block_m, Plan *p) {
     if (req_splits < 0) return fail(RINGATTN_EINVAL, "requested n_splits must be >= 0");
     if (req_block_m != 0 && req_block_m != 128 && req_block_m != 256)
         return fail(RINGATTN_EINVAL, "block_m must be 0 (choose), 128 or 256 (got %d)", req_block_m);
-    const int32_t cap = ct.n_tiles < 1 ? 1 : (ct.n_tiles < kMaxSplits ? ct.n_tiles : kMaxSplits);
     double best = 1e300;
     p->block_m = 0;
     p->n_splits = 1;
     for (int bm : {256, 128}) {
         if (req_block_m != 0 && bm != req_block_m) continue;
+        const int32_t n_tiles = bm == 256 ? L.ct.n_tiles : L.ct32.n_tiles;
+        const int32_t cap = n_tiles < 1 ? 1 : (n_tiles < kMaxSplits ? n_tiles : kMaxSplits);
         const int lo = req_splits > 0 ? (req_splits < cap ? req_splits : cap) : 1;
         const int hi = req_splits > 0 ? lo : cap;
         for (int sp = lo; sp <= hi; ++sp) {
-            const double c = plan_cost(s, ct.n_tiles, bm, sp);
+            const double c = plan_cost(s, n_tiles, bm, sp);
             if (c < best * 0.999) {
                 best = c;
                 p->block_m = bm;
@@ -210,10 +220,14 @@ int make_plan(const ringattn_shape *s, const ChunkTable &ct, int32_t req_splits,
     return RINGATTN_OK;
 }
 
-hipError_t launch_plan(const AttnArgs &a, const Plan &p, int head_dim, EpilogueMode mode, bool chunked,
-                       hipStream_t s) {
-    if (p.block_m == 256) return launch_attn_pp(a, head_dim, mode, chunked, s);
-    return launch_attn(a, head_dim, mode, s);
+// Launch the planned kernel with the tile walk of its tile size.
+hipError_t launch_plan(AttnArgs a, const Plan &p, const Layout &L, int head_dim, EpilogueMode mode, hipStream_t s) {
+    if (p.block_m == 256) {
+        a.ct = L.ct;
+        return launch_attn_pp(a, head_dim, mode, L.chunked, s);
+    }
+    a.ct = L.ct32;
+    return launch_attn_w3(a, head_dim, mode, L.chunked, s);
 }
 
 void fill_common(AttnArgs *a, const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,
@@ -299,13 +313,13 @@ int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_
     const int64_t offs[2] = {0, shape->kv_len};
     if ((st = build_layout(offs, 1, 0, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, L.ct, 1, 0, &p))) return st;
+    if ((st = make_plan(shape, L, 1, 0, &p))) return st;
     fill_common(&a, q, k_chunk, v_chunk, out_acc, lse_acc, scale, shape);
     a.ct = L.ct;
     a.kv_rows = L.kv_rows;
     a.n_qtiles = p.n_qtiles;
     a.n_splits = 1;
-    return check_hip(launch_plan(a, p, shape->head_dim, kModeAccum, L.chunked, (hipStream_t)stream),
+    return check_hip(launch_plan(a, p, L, shape->head_dim, kModeAccum, (hipStream_t)stream),
                      "attention launch");
 }
 
@@ -330,7 +344,7 @@ int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offs
     Layout L;
     if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, L.ct, plan->n_splits, plan->block_m, &p))) return st;
+    if ((st = make_plan(shape, L, plan->n_splits, plan->block_m, &p))) return st;
     plan->n_splits = p.n_splits;
     plan->block_m = p.block_m;
     plan->workspace_bytes = p.ws_bytes;
@@ -352,7 +366,7 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     Layout L;
     if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, L.ct, plan ? plan->n_splits : 0, plan ? plan->block_m : 0, &p))) return st;
+    if ((st = make_plan(shape, L, plan ? plan->n_splits : 0, plan ? plan->block_m : 0, &p))) return st;
     a.ct = L.ct;
     if (a.ct.n_tiles > 0) {
         if ((st = check_ptr(k, 16, "k"))) return st;
@@ -375,7 +389,7 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     a.n_qtiles = p.n_qtiles;
     a.n_splits = p.n_splits;
     if (p.n_splits == 1)
-        return check_hip(launch_plan(a, p, shape->head_dim, kModeFinal, L.chunked, s), "attention launch");
+        return check_hip(launch_plan(a, p, L, shape->head_dim, kModeFinal, s), "attention launch");
 
     float *part_out = static_cast<float *>(workspace);
     uintptr_t lse_addr = reinterpret_cast<uintptr_t>(part_out + (size_t)p.n_splits * p.split_out_stride);
@@ -385,7 +399,7 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
     a.lse = part_lse;
     a.split_out_stride = p.split_out_stride;
     a.split_lse_stride = p.split_lse_stride;
-    if ((st = check_hip(launch_plan(a, p, shape->head_dim, kModePartial, L.chunked, s), "attention launch")))
+    if ((st = check_hip(launch_plan(a, p, L, shape->head_dim, kModePartial, s), "attention launch")))
         return st;
     MergeSplitsArgs m;
     m.part_out = part_out;
@@ -440,7 +454,7 @@ int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v,
             const int64_t offs[2] = {0, len};
             if ((st = build_layout(offs, 1, 0, len, &cl))) return st;
             Plan p;
-            if ((st = make_plan(&rs, cl.ct, 1, 0, &p))) return st;
+            if ((st = make_plan(&rs, cl, 1, 0, &p))) return st;
             AttnArgs a;
             std::memset(&a, 0, sizeof a);
             fill_common(&a, q + q0 * HD, k + row0 * HD, v + row0 * HD, out + q0 * HD, lse + q0, scale, &rs);
@@ -450,7 +464,7 @@ int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v,
             a.kv_rows = L.kv_rows;
             a.n_qtiles = p.n_qtiles;
             a.n_splits = 1;
-            if ((st = check_hip(launch_plan(a, p, shape->head_dim, kModeAccum, cl.chunked, s), "attention launch")))
+            if ((st = check_hip(launch_plan(a, p, cl, shape->head_dim, kModeAccum, s), "attention launch")))
                 return st;
         }
     }
@@ -526,7 +540,7 @@ int ringattn_step_bf16(const uint16_t *q, const uint16_t *k_chunk, const uint16_
     const int64_t offs[2] = {0, shape->kv_len};
     if ((st = build_layout(offs, 1, 0, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, L.ct, 1, 256, &p))) return st;  // the 8-wave kernel has the bf16 epilogue
+    if ((st = make_plan(shape, L, 1, 0, &p))) return st;
     AttnArgs a;
     std::memset(&a, 0, sizeof a);
     fill_common(&a, q, k_chunk, v_chunk, reinterpret_cast<float *>(out_acc), reinterpret_cast<float *>(lse_acc),
@@ -535,7 +549,7 @@ int ringattn_step_bf16(const uint16_t *q, const uint16_t *k_chunk, const uint16_
     a.kv_rows = L.kv_rows;
     a.n_qtiles = p.n_qtiles;
     a.n_splits = 1;
-    return check_hip(launch_plan(a, p, shape->head_dim, kModeAccumBf16, L.chunked, (hipStream_t)stream),
+    return check_hip(launch_plan(a, p, L, shape->head_dim, kModeAccumBf16, (hipStream_t)stream),
                      "attention launch");
 }
 

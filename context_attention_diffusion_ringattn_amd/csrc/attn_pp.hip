@@ -52,72 +52,6 @@ struct PPGeo {
     static_assert(LPW >= 1 && LPW * kPPWaves * 1024 == TILE, "tile split over waves");
 };
 
-// Workgroup barrier that neither the compiler's scheduler nor its memory
-// optimisations move anything across, and that (unlike __syncthreads) does
-// not wait for the in-flight global->LDS loads of later tiles.
-__device__ __forceinline__ void wg_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-typedef __attribute__((address_space(3))) unsigned char lds_byte;
-
-// A value the compiler cannot see through (no instruction is emitted).
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
-// LDS reads at a lane base address plus a constant offset (folded into the
-// instruction's 16-bit offset field).
-__device__ __forceinline__ bf16x8 lds_b128_at(uint32_t base, uint32_t off) {
-    return *(const bf16x8 *)((const lds_byte *)base + off);
-}
-__device__ __forceinline__ s16x4 lds_tr_at(uint32_t base, uint32_t off) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)((lds_byte *)base + off));
-}
-
-// Direct global->LDS load of 16 bytes per lane: lane l's 16 bytes from
-// gbase + voff land at LDS address lds_dst + 16 l (lds_dst wave-uniform, in
-// M0).  Written as inline assembly on purpose: with the builtin in the loop,
-// the compiler treats every LDS read as completing out of order and waits for
-// all of them before each use; hidden from it, the LDS reads get exact
-// counts.  Completion is tracked by vmcnt, which this kernel waits on
-// explicitly before the barrier that publishes a tile.  The "memory" clobber
-// tells the compiler LDS (and anything else) may change here.
-__device__ __forceinline__ void dma_load16(const unsigned char *gbase, uint32_t voff, uint32_t lds_dst) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_dst), "v"(voff), "s"(gbase)
-                 : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// The value of lane i ^ 32 (the other half of the wave).
-// v_permlane32_swap_b32 exchanges the upper 32 lanes of its first operand
-// with the lower 32 lanes of its second: for inputs (a, b) it leaves
-// a' = [a_lo, b_lo] and b' = [a_hi, b_hi]; with a = b = x, lane i then holds
-// x[i ^ 32] in b' (lower lanes) or a' (upper lanes).  It is issued as inline
-// assembly because the compiler's builtin folding drops one of the two
-// results when they feed a floating-point max or add.  The s_nop pairs cover
-// the VALU-write -> permlane-read hazard before and the permlane-write ->
-// VALU-read hazard after, which the hazard recognizer cannot see through
-// inline assembly.
-__device__ __forceinline__ float other_half(float x, bool upper) {
-    float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    return upper ? a : b;
-}
-
 template <int D, int MODE, bool CHUNKED>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pp_kernel(const AttnArgs a) {
@@ -426,97 +360,7 @@ void attn_pp_kernel(const AttnArgs a) {
     // ---- epilogue -------------------------------------------------------------
     const float l_lane = (l0 + l1) + (l2 + l3);
     const float l_tot = l_lane + other_half(l_lane, half != 0);
-    if (qrow >= a.q_len) return;
-    const bool any_keys = T > 0;
-    if ((MODE == kModeAccum || MODE == kModeAccumBf16) && !any_keys) return;
-
-    float *orow = a.out + ((int64_t)b * a.q_pitch + qrow) * HD + (int64_t)h * D + 4 * half;
-    float *lptr = a.lse + ((int64_t)b * a.heads + h) * a.lse_pitch + qrow;
-    if (MODE == kModePartial) {
-        orow += (int64_t)split * a.split_out_stride;
-        lptr += (int64_t)split * a.split_lse_stride;
-    }
-    const float inv_l = any_keys ? 1.f / l_tot : 0.f;
-    const float lse_chunk = any_keys ? fmaf(m_run, a.scale, logf(l_tot)) : -INFINITY;
-
-    if (MODE == kModeAccumBf16) {
-        // Accumulators kept in bf16 between steps: the partial is rounded to
-        // bf16 (as a bf16-output attention pass returns it), merged in
-        // float32 with the stored state, and the result rounded back.
-        uint16_t *o16 = (uint16_t *)a.out + ((int64_t)b * a.q_pitch + qrow) * HD + (int64_t)h * D + 4 * half;
-        uint16_t *l16 = (uint16_t *)a.lse + ((int64_t)b * a.heads + h) * a.lse_pitch + qrow;
-        const float lc = (float)(__bf16)lse_chunk;
-        const float la = (float)__builtin_bit_cast(__bf16, *l16);
-        float wa, wb, lse_new;
-        if (la == -INFINITY) {
-            wa = 0.f;
-            wb = 1.f;
-            lse_new = lc;
-        } else {
-            lse_new = fmaxf(la, lc) + log1pf(expf(-fabsf(la - lc)));
-            wa = expf(la - lse_new);
-            wb = expf(lc - lse_new);
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint16_t *p = o16 + 32 * db + 8 * g;
-                const uint2 cur = *(const uint2 *)p;
-                float r[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float part = (float)(__bf16)(o[db][4 * g + e] * inv_l);
-                    const uint32_t word = e < 2 ? cur.x : cur.y;
-                    const uint16_t bits = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
-                    const float acc = (float)__builtin_bit_cast(__bf16, bits);
-                    r[e] = la == -INFINITY ? part : fmaf(wa, acc, wb * part);
-                }
-                uint2 res;
-                res.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[0]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[1]) << 16);
-                res.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[2]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)r[3]) << 16);
-                *(uint2 *)p = res;
-            }
-        }
-        if (half == 0) *l16 = __builtin_bit_cast(uint16_t, (__bf16)lse_new);
-    } else if (MODE == kModeAccum) {
-        const float la = *lptr;
-        float wa, wb, lse_new;
-        if (la == -INFINITY) {
-            wa = 0.f;
-            wb = 1.f;
-            lse_new = lse_chunk;
-        } else {
-            lse_new = fmaxf(la, lse_chunk) + log1pf(expf(-fabsf(la - lse_chunk)));
-            wa = expf(la - lse_new);
-            wb = expf(lse_chunk - lse_new);
-        }
-        wb *= inv_l;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 *p = (f32x4 *)(orow + 32 * db + 8 * g);
-                const f32x4 cur = f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-                f32x4 res = cur * wb;
-                if (la != -INFINITY) res += wa * (*p);
-                *p = res;
-            }
-        }
-        if (half == 0) *lptr = lse_new;
-    } else {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                *(f32x4 *)(orow + 32 * db + 8 * g) =
-                    f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]} * inv_l;
-            }
-        }
-        if (half == 0) *lptr = lse_chunk;
-    }
+    write_rows<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow, split, half);
 }
 
 template <int D, bool CHUNKED>

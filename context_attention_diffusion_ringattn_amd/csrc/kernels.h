@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI host code (api.cpp) and the gfx950
-// kernels (attn_fwd.hip, merge.hip).  Not installed; not part of the ABI.
+// kernels (attn_pp.hip, attn_w3.hip, merge.hip).  Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,9 +8,7 @@
 namespace ringattn {
 
 constexpr int kMaxChunks = 128;   // == RINGATTN_MAX_CHUNKS
-constexpr int kBlockM = 128;      // query rows per workgroup (4 waves x 32 rows)
-constexpr int kBlockN = 64;       // key/value rows per LDS tile
-constexpr int kThreads = 256;     // 4 wavefronts of 64
+constexpr int kBlockN = 64;       // key/value rows per LDS tile of the 8-wave kernel
 constexpr int kMaxSplits = 32;
 
 // The K/V tiles of one forward call, chunk by chunk.  A tile never straddles
@@ -65,7 +63,9 @@ struct MergeSplitsArgs {
     int64_t split_lse_stride;
 };
 
-hipError_t launch_attn(const AttnArgs &a, int head_dim, EpilogueMode mode, hipStream_t stream);
+// 4-wave, 128-row variant (three workgroups per CU, 32-key tiles; the chunk
+// table counts 32-key tiles).
+hipError_t launch_attn_w3(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream);
 // 8-wave, 256-row variant; `chunked` = walk the chunk table (padded layout).
 hipError_t launch_attn_pp(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream);
 hipError_t launch_merge_splits(const MergeSplitsArgs &a, int head_dim, hipStream_t stream);

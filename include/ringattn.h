@@ -130,12 +130,14 @@ int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const 
  * Launch plan of ringattn_forward.
  *   n_splits: number of key/value splits -- independent partial passes over
  *     disjoint ranges of K/V tiles, merged at the end by their LSE;
- *   block_m: query rows per workgroup, 128 (4 waves) or 256 (8 waves in two
- *     groups that alternate MFMA and softmax phases);
+ *   block_m: query rows per workgroup, 128 (4 waves, three workgroups per
+ *     compute unit, 32-key tiles) or 256 (8 waves in two groups that
+ *     alternate MFMA and softmax phases, 64-key tiles);
  *   workspace_bytes: device workspace the plan needs (0 when n_splits is 1).
  * On input n_splits and block_m are requests (0 = the library chooses from
  * the shape and the GPU's compute-unit count; n_splits > 0 is clamped to the
- * K/V tile count); on output they hold what ringattn_forward will use.
+ * K/V tile count of the chosen kernel); on output they hold what
+ * ringattn_forward will use.
  */
 typedef struct ringattn_plan {
     int32_t n_splits;

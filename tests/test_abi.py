@@ -200,8 +200,9 @@ def test_forward_workspace_error(L):
 
 def test_forward_plan_properties(L):
     """Plans: a single split needs no workspace; splits never exceed the number
-    of K/V tiles (packed chunks form one key range, padded chunks are tiled
-    one by one); block_m is 128 or 256; the plan is deterministic and a
+    of K/V tiles of the chosen kernel (64 keys for block_m 256, 32 for 128;
+    packed chunks form one key range, padded chunks are tiled one by one);
+    block_m is 128 or 256; the plan is deterministic and a
     request for either block size is honoured."""
     for (B, H, D, Sq, offs, stride) in ((1, 24, 128, 8192, oracle.chunk_offsets(65536, 8), 0),
                                         (1, 24, 128, 1152, oracle.chunk_offsets(4608, 4), 0),
@@ -213,10 +214,11 @@ def test_forward_plan_properties(L):
         s = shape(B=B, H=H, D=D, Sq=Sq, Skv=offs[-1])
         st, plan = _plan(L, s, offs, stride=stride)
         assert st == 0
+        n = 64 if plan.block_m == 256 else 32  # keys per tile of the chosen kernel
         if stride:
-            tiles = sum(-(-(b - a) // 64) for a, b in zip(offs, offs[1:]))
+            tiles = sum(-(-(b - a) // n) for a, b in zip(offs, offs[1:]))
         else:
-            tiles = -(-offs[-1] // 64)
+            tiles = -(-offs[-1] // n)
         assert 1 <= plan.n_splits <= max(1, tiles)
         assert plan.block_m in (128, 256)
         assert (plan.workspace_bytes == 0) == (plan.n_splits == 1)
