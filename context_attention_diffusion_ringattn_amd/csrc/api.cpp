@@ -439,6 +439,40 @@ int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     const int64_t n_lse = (int64_t)shape->batch * shape->heads * S;
     if ((st = check_hip(launch_acc_init(out, lse, n_out, n_lse, s), "acc_init launch"))) return st;
 
+    if (n_chunks <= kMaxSweepRanks) {
+        // One launch per ring step s: every rank's query rows with its chunk
+        // (r + s) mod N, merged into its rows in place.
+        for (int step = 0; step < n_chunks; ++step) {
+            AttnArgs a;
+            std::memset(&a, 0, sizeof a);
+            fill_common(&a, q, k, v, out, lse, scale, shape);
+            a.q_pitch = S;
+            a.lse_pitch = S;
+            a.kv_rows = L.kv_rows;
+            a.n_splits = 1;
+            int nr = 0;
+            int64_t tiles = 0;
+            for (int r = 0; r < n_chunks; ++r) {
+                const int64_t q_len = chunk_offsets[r + 1] - chunk_offsets[r];
+                const int c = (r + step) % n_chunks;
+                const int64_t len = chunk_offsets[c + 1] - chunk_offsets[c];
+                if (q_len == 0 || len == 0) continue;  // an empty rank or chunk changes nothing
+                a.rank_q_begin[nr] = chunk_offsets[r];
+                a.rank_q_len[nr] = (int32_t)q_len;
+                a.ct.row_start[nr] = kv_chunk_stride > 0 ? (int64_t)c * kv_chunk_stride : chunk_offsets[c];
+                a.ct.len[nr] = (int32_t)len;
+                tiles += (q_len + 255) / 256;
+                a.rank_qtile_start[nr + 1] = (int32_t)tiles;
+                ++nr;
+            }
+            if (nr == 0) continue;
+            if (tiles * shape->heads * shape->batch > INT32_MAX) return fail(RINGATTN_EINVAL, "grid too large");
+            a.n_ranks = nr;
+            a.ct.n_chunks = nr;
+            if ((st = check_hip(launch_attn_pp_multi(a, shape->head_dim, s), "attention launch"))) return st;
+        }
+        return ok();
+    }
     for (int r = 0; r < n_chunks; ++r) {
         const int64_t q0 = chunk_offsets[r], q_len = chunk_offsets[r + 1] - chunk_offsets[r];
         if (q_len == 0) continue;

@@ -52,7 +52,7 @@ struct PPGeo {
     static_assert(LPW >= 1 && LPW * kPPWaves * 1024 == TILE, "tile split over waves");
 };
 
-template <int D, int MODE, bool CHUNKED>
+template <int D, int MODE, bool CHUNKED, bool MULTI>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pp_kernel(const AttnArgs a) {
     using G = PPGeo<D>;
@@ -70,21 +70,42 @@ void attn_pp_kernel(const AttnArgs a) {
 
     // ---- work assignment ------------------------------------------------
     int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt = w % a.n_qtiles;
-    w /= a.n_qtiles;
-    const int h = w % a.heads;
-    w /= a.heads;
-    const int b = w % a.batch;
-    const int split = w / a.batch;
-    const int t_lo = (int)((int64_t)split * a.ct.n_tiles / a.n_splits);
-    const int t_hi = (int)((int64_t)(split + 1) * a.ct.n_tiles / a.n_splits);
+    int qt, h, b, split, t_lo, t_hi, len0;
+    int64_t q_first = 0, q_end = a.q_len, kv_first = 0;
+    if constexpr (MULTI) {
+        // one ring step of several ranks: find this tile's rank
+        const int total = a.rank_qtile_start[a.n_ranks];
+        const int g = w % total;
+        w /= total;
+        h = w % a.heads;
+        b = w / a.heads;
+        int r = 0;
+        while (g >= a.rank_qtile_start[r + 1]) ++r;
+        qt = g - a.rank_qtile_start[r];
+        q_first = a.rank_q_begin[r];
+        q_end = q_first + a.rank_q_len[r];
+        kv_first = a.ct.row_start[r];
+        len0 = a.ct.len[r];
+        split = 0;
+        t_lo = 0;
+        t_hi = (len0 + kBlockN - 1) / kBlockN;
+    } else {
+        qt = w % a.n_qtiles;
+        w /= a.n_qtiles;
+        h = w % a.heads;
+        w /= a.heads;
+        b = w % a.batch;
+        split = w / a.batch;
+        t_lo = (int)((int64_t)split * a.ct.n_tiles / a.n_splits);
+        t_hi = (int)((int64_t)(split + 1) * a.ct.n_tiles / a.n_splits);
+        len0 = a.ct.len[0];  // packed layout: the whole key range
+    }
     const int T = t_hi - t_lo;
-    const int len0 = a.ct.len[0];  // packed layout: the whole key range
 
     const int64_t HD = (int64_t)a.heads * D;
     const uint32_t row_stride = (uint32_t)(HD * 2);  // bytes between consecutive K/V rows
-    const unsigned char *kbase = (const unsigned char *)(a.k + (int64_t)b * a.kv_rows * HD + (int64_t)h * D);
-    const unsigned char *vbase = (const unsigned char *)(a.v + (int64_t)b * a.kv_rows * HD + (int64_t)h * D);
+    const unsigned char *kbase = (const unsigned char *)(a.k + ((int64_t)b * a.kv_rows + kv_first) * HD + (int64_t)h * D);
+    const unsigned char *vbase = (const unsigned char *)(a.v + ((int64_t)b * a.kv_rows + kv_first) * HD + (int64_t)h * D);
 
     int c_ld = 0, c_sm = 0;  // chunk cursors of the two tile walks (chunked layout)
     auto tile_at = [&](int t, int &c, int64_t &row0, int &nv) __attribute__((always_inline)) {
@@ -97,8 +118,8 @@ void attn_pp_kernel(const AttnArgs a) {
     };
 
     // ---- Q operand (registers for the whole sweep) --------------------------
-    const int64_t qrow = (int64_t)qt * kPPBlockM + wave * 32 + col;
-    const int64_t qrow_ld = qrow < a.q_len ? qrow : a.q_len - 1;
+    const int64_t qrow = q_first + (int64_t)qt * kPPBlockM + wave * 32 + col;
+    const int64_t qrow_ld = qrow < q_end ? qrow : q_end - 1;
     const uint16_t *qp = a.q + ((int64_t)b * a.q_pitch + qrow_ld) * HD + (int64_t)h * D + 8 * half;
     bf16x8 qreg[D / 16];
 #pragma unroll
@@ -360,7 +381,7 @@ void attn_pp_kernel(const AttnArgs a) {
     // ---- epilogue -------------------------------------------------------------
     const float l_lane = (l0 + l1) + (l2 + l3);
     const float l_tot = l_lane + other_half(l_lane, half != 0);
-    write_rows<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow, split, half);
+    write_rows<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow, q_end, split, half);
 }
 
 template <int D, bool CHUNKED>
@@ -368,19 +389,19 @@ hipError_t launch_pp_dc(const AttnArgs &a, EpilogueMode mode, hipStream_t stream
     const int64_t grid = (int64_t)a.n_qtiles * a.heads * a.batch * a.n_splits;
     switch (mode) {
         case kModeFinal:
-            hipLaunchKernelGGL((attn_pp_kernel<D, kModeFinal, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModeFinal, CHUNKED, false>), dim3((unsigned)grid), dim3(kPPThreads), 0,
                                stream, a);
             break;
         case kModePartial:
-            hipLaunchKernelGGL((attn_pp_kernel<D, kModePartial, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModePartial, CHUNKED, false>), dim3((unsigned)grid), dim3(kPPThreads), 0,
                                stream, a);
             break;
         case kModeAccum:
-            hipLaunchKernelGGL((attn_pp_kernel<D, kModeAccum, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModeAccum, CHUNKED, false>), dim3((unsigned)grid), dim3(kPPThreads), 0,
                                stream, a);
             break;
         case kModeAccumBf16:
-            hipLaunchKernelGGL((attn_pp_kernel<D, kModeAccumBf16, CHUNKED>), dim3((unsigned)grid), dim3(kPPThreads),
+            hipLaunchKernelGGL((attn_pp_kernel<D, kModeAccumBf16, CHUNKED, false>), dim3((unsigned)grid), dim3(kPPThreads),
                                0, stream, a);
             break;
     }
@@ -388,6 +409,17 @@ hipError_t launch_pp_dc(const AttnArgs &a, EpilogueMode mode, hipStream_t stream
 }
 
 }  // namespace
+
+hipError_t launch_attn_pp_multi(const AttnArgs &a, int head_dim, hipStream_t stream) {
+    const int64_t grid = (int64_t)a.rank_qtile_start[a.n_ranks] * a.heads * a.batch;
+    if (head_dim == 128)
+        hipLaunchKernelGGL((attn_pp_kernel<128, kModeAccum, false, true>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((attn_pp_kernel<64, kModeAccum, false, true>), dim3((unsigned)grid), dim3(kPPThreads), 0,
+                           stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_pp(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream) {
     if (head_dim == 128) return chunked ? launch_pp_dc<128, true>(a, mode, stream) : launch_pp_dc<128, false>(a, mode, stream);

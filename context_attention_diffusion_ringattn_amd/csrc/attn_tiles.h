@@ -152,7 +152,8 @@ __device__ __forceinline__ float other_half(float x, bool upper) {
 }
 
 // Epilogue shared by the streaming kernels: one lane's 4*D/32 outputs of
-// query row `qrow` (head h, batch b) and, from the lower half, its LSE.
+// query row `qrow` (head h, batch b; rows at or past q_end are not written)
+// and, from the lower half, its LSE.
 //   Final: out = O / l, lse = m*scale + ln l.
 //   Partial: the same into K/V-split slot `split` of the workspace.
 //   Accum: LSE-merge (out, lse) into the float32 accumulators in place; where
@@ -161,9 +162,10 @@ __device__ __forceinline__ float other_half(float x, bool upper) {
 // With no keys at all the result is out = 0, lse = -inf (merge modes: no-op).
 template <int D, int MODE>
 __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[D / 32], float m_run, float l_tot,
-                                           bool any_keys, int b, int h, int64_t qrow, int split, int half) {
+                                           bool any_keys, int b, int h, int64_t qrow, int64_t q_end, int split,
+                                           int half) {
     const int64_t HD = (int64_t)a.heads * D;
-    if (qrow >= a.q_len) return;
+    if (qrow >= q_end) return;
     if ((MODE == kModeAccum || MODE == kModeAccumBf16) && !any_keys) return;
 
     float *orow = a.out + ((int64_t)b * a.q_pitch + qrow) * HD + (int64_t)h * D + 4 * half;

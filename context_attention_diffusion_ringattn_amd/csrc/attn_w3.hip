@@ -268,7 +268,7 @@ void attn_w3_kernel(const AttnArgs a) {
     // ---- epilogue -------------------------------------------------------------
     const float l_lane = l0 + l1;
     const float l_tot = l_lane + other_half(l_lane, half != 0);
-    write_rows<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow, split, half);
+    write_rows<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow, a.q_len, split, half);
 }
 
 template <int D, bool CHUNKED>

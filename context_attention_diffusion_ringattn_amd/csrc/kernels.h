@@ -10,6 +10,7 @@ namespace ringattn {
 constexpr int kMaxChunks = 128;   // == RINGATTN_MAX_CHUNKS
 constexpr int kBlockN = 64;       // key/value rows per LDS tile of the 8-wave kernel
 constexpr int kMaxSplits = 32;
+constexpr int kMaxSweepRanks = 32;  // ranks one batched ring-step launch covers
 
 // The K/V tiles of one forward call, chunk by chunk.  A tile never straddles
 // two chunks: chunk c owns tiles [tile_start[c], tile_start[c+1]), the last of
@@ -48,6 +49,14 @@ struct AttnArgs {
     float scale;               // softmax scale
     float scale_log2e;         // scale * log2(e), for exp2
     ChunkTable ct;
+    // Batched ring step (multi-rank launches only): rank r's query rows
+    // [rank_q_begin[r], +rank_q_len[r]) attend to K/V rows
+    // [ct.row_start[r], +ct.len[r]); its query tiles are workgroup tiles
+    // [rank_qtile_start[r], rank_qtile_start[r+1]).
+    int32_t n_ranks;
+    int32_t rank_qtile_start[kMaxSweepRanks + 1];
+    int32_t rank_q_len[kMaxSweepRanks];
+    int64_t rank_q_begin[kMaxSweepRanks];
 };
 
 struct MergeSplitsArgs {
@@ -68,6 +77,8 @@ struct MergeSplitsArgs {
 hipError_t launch_attn_w3(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream);
 // 8-wave, 256-row variant; `chunked` = walk the chunk table (padded layout).
 hipError_t launch_attn_pp(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream);
+// One ring step of several ranks in one launch (8-wave kernel, in-place float32 merge).
+hipError_t launch_attn_pp_multi(const AttnArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_merge_splits(const MergeSplitsArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_merge2(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
                          int64_t q_len, int32_t batch, int32_t heads, int32_t head_dim, hipStream_t stream);

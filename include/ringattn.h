@@ -199,8 +199,10 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  *     padded Ring Anything buffer (kv_chunk_stride > 0, rows =
  *     n_chunks * kv_chunk_stride; padding rows are never read);
  *   out: [B, S, H, D] float32, lse: [B, H, S] float32, fully written.
- * Enqueues one initialisation and at most n_chunks^2 attention launches on
- * `stream` (none for empty ranks or chunks).  scale must be finite and > 0.
+ * Enqueues one initialisation and, for n_chunks <= 32, one attention launch
+ * per ring step covering every rank (n_chunks^2 launches above 32), on
+ * `stream`; empty ranks and chunks launch nothing.  scale must be finite
+ * and > 0.
  */
 int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         const int64_t *chunk_offsets, int32_t n_chunks, int64_t kv_chunk_stride,

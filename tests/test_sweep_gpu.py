@@ -85,6 +85,8 @@ SMALL_CASES = [
     (1, 2, 128, 5, 8, True, 201),        # 3 empty ranks / chunks
     (1, 1, 128, 1000, 3, True, 202),     # 334, 333, 333: ragged tails
     (3, 2, 128, 520, 4, False, 203),     # 4 x 130
+    (1, 2, 64, 203, 40, True, 204),      # 40 ranks: above the batched-launch limit (per-rank launches)
+    (1, 3, 128, 161, 32, True, 205),     # 32 ranks: the largest batched ring step
 ]
 
 
