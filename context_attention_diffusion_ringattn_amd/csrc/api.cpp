@@ -179,7 +179,7 @@ double plan_cost(const ringattn_shape *s, int32_t n_tiles, int block_m, int spli
     double cost = rounds * (per_wg * tile_us + fixed_us);
     if (splits > 1) {
         const double part_bytes = (double)s->batch * s->q_len * s->heads * (s->head_dim + 1) * 4.0;
-        cost += (2.0 * splits * part_bytes + part_bytes) / 5.0e6 + 4.0;
+        cost += (2.0 * splits * part_bytes + part_bytes) / 5.0e6 + 8.0;  // + the merge launch
     }
     return cost;
 }
