@@ -30,11 +30,16 @@ class RingConfig:
     * ``ulysses_degree``: head groups; with ring_degree = 1 this GPU's share is
       full-sequence attention over heads / ulysses_degree heads;
     * ``convert_to_fp32``: output and LSE merged in float32 (default True, the
-      only mode built);
+      mode of every forward call; the bf16 state exists only per ring step,
+      ``step_bf16``, to measure the error it causes);
     * ``rotate_method``: only ``"allgather"`` is supported (as on the page);
     * ``ring_anything``: uneven chunks; needs ring_degree > 1 and
       ulysses_degree == 1, inference only, no attention mask (guide, variant
-      table and section "Ring Anything Attention").
+      table and section "Ring Anything Attention");
+    * ``ulysses_anything``: uneven sequence and head split over Ulysses; needs
+      ulysses_degree > 1 and ring_degree == 1 (section "Ulysses Anything
+      Attention").
+    ``share(seq_len, heads, rank)`` gives a rank's layout (``cp_share``).
     """
 
     ring_degree: int = 1
@@ -42,18 +47,29 @@ class RingConfig:
     convert_to_fp32: bool = True
     rotate_method: str = "allgather"
     ring_anything: bool = False
+    ulysses_anything: bool = False
 
     def __post_init__(self):
         if self.ring_degree < 1 or self.ulysses_degree < 1:
             raise ValueError("ring_degree and ulysses_degree must be >= 1")
         if not self.convert_to_fp32:
-            raise ValueError("convert_to_fp32=False is not built; the merge is always float32")
+            raise ValueError("convert_to_fp32=False: the forward path always merges in float32 "
+                             "(step_bf16 runs the bf16 state per ring step, for measuring its error)")
         if self.rotate_method != "allgather":
             raise ValueError(f"rotate_method {self.rotate_method!r} is not supported; only 'allgather'")
         if self.ring_anything and (self.ring_degree <= 1 or self.ulysses_degree != 1):
             raise ValueError("ring_anything needs ring_degree > 1 and ulysses_degree == 1")
+        if self.ulysses_anything and (self.ulysses_degree <= 1 or self.ring_degree != 1):
+            raise ValueError("ulysses_anything needs ulysses_degree > 1 and ring_degree == 1")
+        if self.ring_anything and self.ulysses_anything:
+            raise ValueError("ring_anything and ulysses_anything do not combine")
         if self.ring_degree > _lib.RINGATTN_MAX_CHUNKS:
             raise ValueError(f"ring_degree above {_lib.RINGATTN_MAX_CHUNKS} is not supported")
+
+    def share(self, seq_len: int, heads: int, rank: int) -> dict:
+        """The layout of `rank` in this configuration's ring x Ulysses grid."""
+        return cp_share(seq_len, heads, ring_degree=self.ring_degree, ulysses_degree=self.ulysses_degree,
+                        ring_anything=self.ring_anything, ulysses_anything=self.ulysses_anything, rank=rank)
 
 
 # ------------------------------------------------------------- marshalling --
@@ -233,7 +249,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     offsets).  Buffers not passed in are allocated with torch on q's device.
     """
     if not convert_to_fp32:
-        raise ValueError("convert_to_fp32=False is not built; the merge is always float32")
+        raise ValueError("convert_to_fp32=False: the forward path always merges in float32 "
+                         "(step_bf16 runs the bf16 state per ring step, for measuring its error)")
     _check_bf16(q, "q")
     _check_bf16(k, "k")
     _check_bf16(v, "v")

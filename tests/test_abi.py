@@ -253,6 +253,14 @@ def test_python_config_rules():
         RingConfig(ring_degree=2, rotate_method="alltoall")
     with pytest.raises(ValueError):
         RingConfig(ring_degree=0)
+    cfg = RingConfig(ulysses_degree=4, ulysses_anything=True)
+    assert cfg.share(4481, 24, 3) == {"ring_index": 0, "ulysses_index": 3, "token_begin": 3361,
+                                      "token_end": 4481, "q_begin": 0, "q_end": 4481,
+                                      "head_begin": 18, "head_end": 24}
+    with pytest.raises(ValueError):
+        RingConfig(ring_degree=2, ulysses_degree=2, ulysses_anything=True)
+    with pytest.raises(ValueError):
+        RingConfig(ulysses_degree=1, ulysses_anything=True)
 
 
 def test_python_offsets_wrapper():
