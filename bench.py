@@ -40,7 +40,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video",
-                    help="tiny | flux | ring_anything | ulysses | video | usp | ulysses_anything (default: video)")
+                    help="tiny | flux | ring_anything | ring_even | ulysses | ulysses_anything | ulysses_even | usp | video (default: video)")
     ap.add_argument("--splits", type=int, default=0, help="force the K/V split count (0 = library plan)")
     ap.add_argument("--block-m", type=int, default=0, help="force query rows per workgroup, 128 or 256 "
                                                             "(0 = library plan)")

@@ -94,6 +94,16 @@ WORKLOADS: Dict[str, Workload] = {
         description="Ulysses Anything share of FLUX at 1008x1008 on 4 GPUs: S=4481 (3969 image + 512 text "
                     "tokens, not divisible by 4), 24 heads / 4 = 6 heads per GPU, one full non-causal "
                     "pass, B=1 D=128, bf16 N(0,1)"),
+    "ring_even": Workload(
+        "ring_even", batch=1, heads=24, head_dim=128, seq_len=4608, n_chunks=8, ring_anything=False,
+        q_rows=576, seed=7, k_outlier_frac=0.01, k_outlier_scale=8.0,
+        description="plain ring counterpart of ring_anything: B=1 H=24 D=128 S=4608 in 8 even chunks of "
+                    "576, local Q = first chunk, bf16 N(0,1) with 1% of K rows x8"),
+    "ulysses_even": Workload(
+        "ulysses_even", batch=1, heads=6, head_dim=128, seq_len=4608, n_chunks=1, ring_anything=False,
+        q_rows=4608, seed=8,
+        description="plain Ulysses counterpart of ulysses_anything: FLUX at 1024x1024 on 4 GPUs, S=4608, "
+                    "24 heads / 4 = 6 heads per GPU, one full non-causal pass, B=1 D=128, bf16 N(0,1)"),
 }
 
 

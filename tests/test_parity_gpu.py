@@ -280,3 +280,50 @@ def test_full_size_sampled(ra, name):
     ref_out, ref_lse = oracle.attention_rows_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]),
                                                   x["scale"], rows)
     assert_close(out[:, rows], lse[:, :, rows], ref_out, ref_lse, f"{name} sampled rows {len(rows)}")
+
+
+def test_invalid_call_writes_nothing(ra):
+    """Every argument error the library reports (bad chunk offsets, a bad
+    scale, a short workspace) is found before any launch: the output and
+    accumulator buffers keep their contents."""
+    x = workload_inputs("tiny")
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    out = torch.full((1, 128, 2, 64), 7.0, dtype=torch.float32, device="cuda:0")
+    lse = torch.full((1, 2, 128), 7.0, dtype=torch.float32, device="cuda:0")
+    qf = dev(x["q_full"])
+    out_f = torch.full((1, 256, 2, 64), 7.0, dtype=torch.float32, device="cuda:0")
+    lse_f = torch.full((1, 2, 256), 7.0, dtype=torch.float32, device="cuda:0")
+    print("case invalid calls", flush=True)
+    for bad in ([0, 200, 100, 256], [1, 128, 256], [0, -1, 256]):
+        with pytest.raises(ra.RingAttnError):
+            ra.forward(q, k, v, chunk_offsets=bad, scale=x["scale"], out=out, lse=lse)
+        with pytest.raises(ra.RingAttnError):
+            ra.ring_sweep(qf, k, v, chunk_offsets=bad, scale=x["scale"], out=out_f, lse=lse_f)
+    for bad_scale in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(ra.RingAttnError):
+            ra.forward(q, k, v, chunk_offsets=[0, 128, 256], scale=bad_scale, out=out, lse=lse)
+    short = torch.empty((16,), dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(ra.RingAttnError):
+        ra.forward(q, k, v, chunk_offsets=[0, 128, 256], scale=x["scale"], n_splits=2, out=out, lse=lse,
+                   workspace=short)
+    acc_o, acc_l = out.clone(), lse.clone()
+    with pytest.raises(ra.RingAttnError):
+        ra.step(q, k[:, :128].contiguous(), v[:, :128].contiguous(), acc_o, acc_l, scale=float("nan"))
+    torch.cuda.synchronize()
+    for t in (out, lse, out_f, lse_f, acc_o, acc_l):
+        assert torch.all(t == 7.0)
+
+
+@pytest.mark.parametrize("name", ["ring_even", "ulysses_even"])
+def test_even_counterparts(ra, name):
+    """The plain-split counterparts of the Ring Anything and Ulysses Anything
+    workloads, compared in full (ring) or on sampled rows (Ulysses)."""
+    x = workload_inputs(name)
+    w = x["workload"]
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    out, lse = ra.forward(q, k, v, ring_degree=w.n_chunks, scale=x["scale"])
+    torch.cuda.synchronize()
+    rows = list(range(w.q_rows)) if name == "ring_even" else sampled_rows(w.q_rows, 24, seed=w.seed)
+    ref_out, ref_lse = oracle.attention_rows_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]),
+                                                  x["scale"], rows)
+    assert_close(out[:, rows], lse[:, :, rows], ref_out, ref_lse, name)
