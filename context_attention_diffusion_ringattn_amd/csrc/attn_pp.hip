@@ -1,11 +1,10 @@
 // attn_pp.hip -- 8-wave ping-pong ring-shard attention kernel for gfx950.
 //
-// Same computation as attn_fwd.hip (one non-causal softmax-attention sweep of
-// a query block over K/V tiles, the running float32 (max, sum, output) state
-// being the log-sum-exp merge of the partials seen so far -- context
-// parallelism guide "Paralelisme konteks", section "Ring Attention";
-// Parallelism API page, ContextParallelConfig.convert_to_fp32), organised for
-// large query shards:
+// One non-causal softmax-attention sweep of a query block over K/V tiles,
+// the running float32 (max, sum, output) state being the log-sum-exp merge of
+// the partials seen so far (context parallelism guide "Paralelisme konteks",
+// section "Ring Attention"; Parallelism API page,
+// ContextParallelConfig.convert_to_fp32), organised for large query shards:
 //
 //  * One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
 //    owns 32 rows.  Every K/V tile brought into LDS is used by all 256 rows.

@@ -16,41 +16,66 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMergeThreads = 256;
 
-// out/lse <- merge over n_splits partial slots.
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const MergeSplitsArgs a) {
-    constexpr int G = D / 4;
-    const int64_t gid = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
-    const int64_t n_rows = (int64_t)a.batch * a.q_len * a.heads;  // (b, i, h) triples
-    if (gid >= n_rows * G) return;
-    const int g = (int)(gid % G);
-    const int64_t bih = gid / G;
-    const int h = (int)(bih % a.heads);
-    const int64_t bi = bih / a.heads;
-    const int64_t i = bi % a.q_len;
-    const int64_t b = bi / a.q_len;
-    const int64_t lse_idx = (b * a.heads + h) * a.q_len + i;
-    const int64_t out_idx = bih * D + 4 * g;
+// out/lse <- merge over n_splits partial slots.  A workgroup owns kMergeSlice
+// consecutive 16-byte pieces of the output (a contiguous range of every
+// partial slot and of out, covering kMergeSlice / (D/4) whole (b, i, h)
+// rows).  One thread per row first reads the row's split LSEs, writes the
+// merged LSE and leaves the split weights exp(l_s - lse) in LDS (0 for an
+// empty split, whose slot is then never read); then every thread merges its
+// pieces.
+constexpr int kMergePer = 2;
+constexpr int kMergeSlice = kMergeThreads * kMergePer;
 
-    float mx = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, a.part_lse[s * a.split_lse_stride + lse_idx]);
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    float lse = -INFINITY;
-    if (mx != -INFINITY) {
-        float sum = 0.f;
-        for (int s = 0; s < a.n_splits; ++s) {
-            const float l = a.part_lse[s * a.split_lse_stride + lse_idx];
-            if (l != -INFINITY) sum += expf(l - mx);
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_slice_kernel(const MergeSplitsArgs a) {
+    constexpr int G = D / 4;
+    constexpr int NP = kMergeSlice / G;  // rows per workgroup
+    __shared__ float w[NP * kMaxSplits];
+    const int NS = a.n_splits;
+    const int64_t n4 = (int64_t)a.batch * a.q_len * a.heads * G;
+    const int64_t e0 = (int64_t)blockIdx.x * kMergeSlice;
+    const int64_t p0 = e0 / G;  // first (b, i, h) row of this workgroup
+    const int np = (int)min((int64_t)NP, n4 / G - p0);
+    if ((int)threadIdx.x < np) {
+        const int64_t bih = p0 + threadIdx.x;
+        const int64_t bi = bih / a.heads;
+        const int h = (int)(bih - bi * a.heads);
+        const int64_t b = bi / a.q_len, i = bi - b * a.q_len;
+        const int64_t lse_idx = (b * a.heads + h) * a.q_len + i;
+        const float *lp = a.part_lse + lse_idx;
+        float mx = -INFINITY;
+        for (int sp = 0; sp < NS; ++sp) mx = fmaxf(mx, lp[sp * a.split_lse_stride]);
+        float lse = -INFINITY;
+        if (mx != -INFINITY) {
+            float sum = 0.f;
+            for (int sp = 0; sp < NS; ++sp) {
+                const float l = lp[sp * a.split_lse_stride];
+                if (l != -INFINITY) sum += expf(l - mx);
+            }
+            lse = mx + logf(sum);
         }
-        lse = mx + logf(sum);
-        for (int s = 0; s < a.n_splits; ++s) {
-            const float l = a.part_lse[s * a.split_lse_stride + lse_idx];
-            if (l == -INFINITY) continue;  // empty split: never multiplied
-            acc += expf(l - lse) * *(const f32x4 *)(a.part_out + s * a.split_out_stride + out_idx);
+        for (int sp = 0; sp < NS; ++sp) {
+            const float l = lp[sp * a.split_lse_stride];
+            w[threadIdx.x * kMaxSplits + sp] = (lse == -INFINITY || l == -INFINITY) ? 0.f : expf(l - lse);
         }
+        a.lse[lse_idx] = lse;
     }
-    *(f32x4 *)(a.out + out_idx) = acc;
-    if (g == 0) a.lse[lse_idx] = lse;
+    __syncthreads();
+    const f32x4 *part = (const f32x4 *)a.part_out;
+    const int64_t stride4 = a.split_out_stride / 4;
+#pragma unroll
+    for (int k = 0; k < kMergePer; ++k) {
+        const int le = k * kMergeThreads + threadIdx.x;
+        const int64_t e = e0 + le;
+        if (e >= n4) break;
+        const float *we = w + (le / G) * kMaxSplits;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < NS; ++sp) {
+            const float ws = we[sp];
+            if (ws != 0.f) acc += ws * part[sp * stride4 + e];
+        }
+        ((f32x4 *)a.out)[e] = acc;
+    }
 }
 
 // acc <- merge(acc, part) in place.
@@ -116,10 +141,11 @@ inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kMergeThreads - 1
 
 hipError_t launch_merge_splits(const MergeSplitsArgs &a, int head_dim, hipStream_t stream) {
     const int64_t n = (int64_t)a.batch * a.q_len * a.heads * (head_dim / 4);
+    const int64_t grid = (n + kMergeSlice - 1) / kMergeSlice;
     if (head_dim == 128)
-        hipLaunchKernelGGL(merge_splits_kernel<128>, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, a);
+        hipLaunchKernelGGL(merge_slice_kernel<128>, dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(merge_splits_kernel<64>, dim3(blocks_for(n)), dim3(kMergeThreads), 0, stream, a);
+        hipLaunchKernelGGL(merge_slice_kernel<64>, dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, a);
     return hipGetLastError();
 }
 
