@@ -380,7 +380,16 @@ void attn_pp_kernel(const AttnArgs a) {
     // ---- epilogue -------------------------------------------------------------
     const float l_lane = (l0 + l1) + (l2 + l3);
     const float l_tot = l_lane + other_half(l_lane, half != 0);
-    write_rows<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow, q_end, split, half);
+    if constexpr (D == 128 && (MODE == kModeFinal || MODE == kModePartial)) {
+        // The K stages are free: the last QK phase ended before the barrier
+        // both groups passed on their way here (V of the last tile may still
+        // be read by the trailing group).
+        static_assert(kPPWaves * kStageBytes <= 4 * G::TILE, "staging fits the K stages");
+        write_rows_staged<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow - col, q_end, split, lane,
+                                   lds0 + kKRegion + (uint32_t)wave * kStageBytes);
+    } else {
+        write_rows<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow, q_end, split, half);
+    }
 }
 
 template <int D, bool CHUNKED>

@@ -257,4 +257,54 @@ __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[
     }
 }
 
+// The final (or split-partial) output of one wave's 32 rows, staged through
+// LDS so that every global store writes whole 128-byte row segments.  In the
+// MFMA layout an f32x4 store covers 32 bytes of each of 32 rows; here the
+// wave writes its rows to `scratch` (kStageRowFloats floats per row, padded
+// against bank conflicts), then each store instruction covers eight rows of
+// 32 consecutive floats.  The LDS exchange stays inside the wave (LDS
+// operations of one wave complete in order), so every lane takes part and
+// only the global stores of rows at or past q_end are skipped.  `row0` is
+// the wave's first query row, `scratch` an LDS byte address of
+// 32 * kStageRowFloats * 4 bytes that no other wave touches.
+constexpr int kStageRowFloats = 36;
+constexpr uint32_t kStageBytes = 32u * kStageRowFloats * 4u;
+
+template <int D, int MODE>
+__device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x16 (&o)[D / 32], float m_run,
+                                                  float l_tot, bool any_keys, int b, int h, int64_t row0,
+                                                  int64_t q_end, int split, int lane, uint32_t scratch) {
+    static_assert(MODE == kModeFinal || MODE == kModePartial, "stores only");
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    const int col = lane & 31, half = lane >> 5;
+    const int64_t HD = (int64_t)a.heads * D;
+    float *obase = a.out + ((int64_t)b * a.q_pitch + row0) * HD + (int64_t)h * D;
+    float *lptr = a.lse + ((int64_t)b * a.heads + h) * a.lse_pitch + row0 + col;
+    if (MODE == kModePartial) {
+        obase += (int64_t)split * a.split_out_stride;
+        lptr += (int64_t)split * a.split_lse_stride;
+    }
+    const float inv_l = any_keys ? 1.f / l_tot : 0.f;
+    const float lse_chunk = any_keys ? fmaf(m_run, a.scale, logf(l_tot)) : -INFINITY;
+    const int rr = lane >> 3;       // read-back row within a group of eight
+    const int c4 = 4 * (lane & 7);  // read-back first column
+    const int64_t rows_left = q_end - row0;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t at = scratch + (uint32_t)(col * kStageRowFloats + 8 * g + 4 * half) * 4u;
+            *(lds_f32x4 *)(uintptr_t)at =
+                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]} * inv_l;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 8 * k + rr;
+            const f32x4 v = *(lds_f32x4 *)(uintptr_t)(scratch + (uint32_t)(r * kStageRowFloats + c4) * 4u);
+            if (r < rows_left) *(f32x4 *)(obase + (int64_t)r * HD + 32 * db + c4) = v;
+        }
+    }
+    if (half == 0 && col < rows_left) *lptr = lse_chunk;
+}
+
 }  // namespace ringattn
