@@ -382,8 +382,10 @@ void attn_pp_kernel(const AttnArgs a) {
     const float l_tot = l_lane + other_half(l_lane, half != 0);
     if constexpr (D == 128 && (MODE == kModeFinal || MODE == kModePartial)) {
         // The K stages are free: the last QK phase ended before the barrier
-        // both groups passed on their way here (V of the last tile may still
-        // be read by the trailing group).
+        // both groups passed on their way here.  The V stages are not: waves
+        // of the trailing group may still read V of the last tile, with no
+        // barrier after it.  At D = 64 the K stages cannot hold the slices of
+        // all eight waves, so that head dim keeps the direct stores.
         static_assert(kPPWaves * kStageBytes <= 4 * G::TILE, "staging fits the K stages");
         write_rows_staged<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow - col, q_end, split, lane,
                                    lds0 + kKRegion + (uint32_t)wave * kStageBytes);

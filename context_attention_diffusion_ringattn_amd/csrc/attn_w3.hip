@@ -268,7 +268,7 @@ void attn_w3_kernel(const AttnArgs a) {
     // ---- epilogue -------------------------------------------------------------
     const float l_lane = l0 + l1;
     const float l_tot = l_lane + other_half(l_lane, half != 0);
-    if constexpr (D == 128 && (MODE == kModeFinal || MODE == kModePartial)) {
+    if constexpr (MODE == kModeFinal || MODE == kModePartial) {
         // every wave passed the barrier after the last tile: the stages are free
         static_assert(kW3Waves * kStageBytes <= sizeof(smem), "staging fits the stages");
         write_rows_staged<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow - col, a.q_len, split, lane,
