@@ -101,6 +101,11 @@ def _check_f32(t: torch.Tensor, name: str, shape: Tuple[int, ...], device: torch
         raise ValueError(f"{name} must be on {device} (got {t.device})")
 
 
+def _check_device(t: torch.Tensor, name: str, device: torch.device) -> None:
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, the device of q (got {t.device})")
+
+
 def _shape(q: torch.Tensor, kv_len: int) -> Shape:
     B, Sq, H, D = q.shape
     return Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=kv_len)
@@ -132,7 +137,12 @@ _library_chunk_offsets = chunk_offsets
 
 def acc_init(out_acc: torch.Tensor, lse_acc: torch.Tensor, stream=None) -> None:
     """Set accumulators to the empty state (out = 0, lse = -inf)."""
+    if not isinstance(out_acc, torch.Tensor) or out_acc.dim() != 4:
+        raise ValueError("out_acc must be a [batch, seq, heads, head_dim] tensor")
+    if out_acc.device.type != "cuda":
+        raise ValueError(f"out_acc must be on a ROCm device (got {out_acc.device})")
     B, Sq, H, D = out_acc.shape
+    _check_f32(out_acc, "out_acc", (B, Sq, H, D), out_acc.device)
     _check_f32(lse_acc, "lse_acc", (B, H, Sq), out_acc.device)
     shape = Shape(batch=B, heads=H, head_dim=D, reserved=0, q_len=Sq, kv_len=0)
     check(lib().ringattn_acc_init(_ptr(out_acc), _ptr(lse_acc), ctypes.byref(shape),
@@ -158,6 +168,8 @@ def step(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out_acc:
     B, Sq, H, D = q.shape
     if k_chunk.shape != v_chunk.shape or k_chunk.shape[0] != B or k_chunk.shape[2:] != q.shape[2:]:
         raise ValueError(f"k/v chunk shapes {tuple(k_chunk.shape)} / {tuple(v_chunk.shape)} do not match q")
+    _check_device(k_chunk, "k_chunk", q.device)
+    _check_device(v_chunk, "v_chunk", q.device)
     _check_f32(out_acc, "out_acc", (B, Sq, H, D), q.device)
     _check_f32(lse_acc, "lse_acc", (B, H, Sq), q.device)
     if scale is None:
@@ -190,6 +202,8 @@ def step_bf16(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out
     B, Sq, H, D = q.shape
     if k_chunk.shape != v_chunk.shape or k_chunk.shape[0] != B or k_chunk.shape[2:] != q.shape[2:]:
         raise ValueError(f"k/v chunk shapes {tuple(k_chunk.shape)} / {tuple(v_chunk.shape)} do not match q")
+    _check_device(k_chunk, "k_chunk", q.device)
+    _check_device(v_chunk, "v_chunk", q.device)
     for t, name, shp in ((out_acc, "out_acc", (B, Sq, H, D)), (lse_acc, "lse_acc", (B, H, Sq))):
         if t.dtype != torch.bfloat16 or tuple(t.shape) != shp or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shp} on {q.device}")
@@ -204,6 +218,10 @@ def step_bf16(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out
 def merge(out_acc: torch.Tensor, lse_acc: torch.Tensor, out_part: torch.Tensor, lse_part: torch.Tensor,
           stream=None) -> None:
     """LSE-merge a float32 partial into the accumulators in place."""
+    if not isinstance(out_acc, torch.Tensor) or out_acc.dim() != 4:
+        raise ValueError("out_acc must be a [batch, seq, heads, head_dim] tensor")
+    if out_acc.device.type != "cuda":
+        raise ValueError(f"out_acc must be on a ROCm device (got {out_acc.device})")
     B, Sq, H, D = out_acc.shape
     _check_f32(out_acc, "out_acc", (B, Sq, H, D), out_acc.device)
     _check_f32(out_part, "out_part", (B, Sq, H, D), out_acc.device)
@@ -257,6 +275,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     B, Sq, H, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
         raise ValueError(f"k/v shapes {tuple(k.shape)} / {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    _check_device(k, "k", q.device)
+    _check_device(v, "v", q.device)
     if chunk_offsets is None:
         if ring_degree is None:
             ring_degree = 1
@@ -285,6 +305,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                                           ctypes.byref(plan)), "ringattn_forward_plan")
         if plan.workspace_bytes:
             workspace = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor")
+        _check_device(workspace, "workspace", q.device)
     ws_ptr = _ptr(workspace)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(lib().ringattn_forward(_ptr(q), _ptr(k), _ptr(v), arr, n_chunks, int(kv_chunk_stride), _ptr(out), _ptr(lse),
@@ -315,6 +339,8 @@ def ring_sweep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     B, S, H, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
         raise ValueError(f"k/v shapes {tuple(k.shape)} / {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    _check_device(k, "k", q.device)
+    _check_device(v, "v", q.device)
     if chunk_offsets is None:
         if kv_chunk_stride:
             raise ValueError("kv_chunk_stride needs explicit chunk_offsets")
