@@ -327,3 +327,35 @@ def test_even_counterparts(ra, name):
     ref_out, ref_lse = oracle.attention_rows_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]),
                                                   x["scale"], rows)
     assert_close(out[:, rows], lse[:, :, rows], ref_out, ref_lse, name)
+
+
+def test_maximum_chunk_count_and_wide_heads(ra):
+    """The largest chunk table the ABI accepts (RINGATTN_MAX_CHUNKS chunks of
+    mixed lengths, some empty) through the packed and the padded layout, and
+    a layer with many heads; both workgroup shapes."""
+    n = ra._lib.RINGATTN_MAX_CHUNKS
+    rng = np.random.default_rng(77)
+    lens = [0 if rng.random() < 0.15 else int(rng.integers(1, 41)) for _ in range(n)]
+    S = sum(lens)
+    offs = [0]
+    for m in lens:
+        offs.append(offs[-1] + m)
+    for B, H, D, Sq in ((1, 3, 128, 300), (2, 40, 64, 70)):
+        print(f"case max chunks: B={B} H={H} D={D} Sq={Sq} S={S} n={n}", flush=True)
+        x = W.make_random(B, Sq, S, H, D, 78 + H, k_outlier_frac=0.02, k_outlier_scale=6.0)
+        ref_out, ref_lse = oracle.attention_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]), x["scale"])
+        q = dev(x["q"])
+        pad = max(lens)
+        kp = torch.full((B, n * pad, H, D), float("nan"), dtype=torch.bfloat16)
+        vp = torch.full((B, n * pad, H, D), float("nan"), dtype=torch.bfloat16)
+        for c in range(n):
+            kp[:, c * pad:c * pad + lens[c]] = x["k"][:, offs[c]:offs[c + 1]]
+            vp[:, c * pad:c * pad + lens[c]] = x["v"][:, offs[c]:offs[c + 1]]
+        for block_m in (128, 256):
+            out, lse = ra.forward(q, dev(x["k"]), dev(x["v"]), chunk_offsets=offs, scale=x["scale"], block_m=block_m)
+            torch.cuda.synchronize()
+            assert_close(out, lse, ref_out, ref_lse, f"max chunks packed block_m={block_m} H={H}")
+            out, lse = ra.forward(q, dev(kp), dev(vp), chunk_offsets=offs, kv_chunk_stride=pad, scale=x["scale"],
+                                  block_m=block_m, n_splits=3)
+            torch.cuda.synchronize()
+            assert_close(out, lse, ref_out, ref_lse, f"max chunks padded block_m={block_m} H={H}")
