@@ -268,3 +268,23 @@ def test_python_offsets_wrapper():
     assert chunk_offsets(4611, 8, ring_anything=True) == oracle.chunk_offsets(4611, 8, ring_anything=True)
     with pytest.raises(RingAttnError):
         chunk_offsets(4481, 4)
+
+
+def test_bf16_state_calls_validate(L):
+    """ringattn_step_bf16 and ringattn_acc_init_bf16 validate like their float32
+    counterparts before any launch; an empty chunk is a no-op."""
+    s = shape()
+    f = ctypes.c_float(0.125)
+    for args in ((None, P, P, P, P), (P, None, P, P, P), (P, P, None, P, P), (P, P, P, None, P), (P, P, P, P, None),
+                 (P_MISALIGNED, P, P, P, P)):
+        assert L.ringattn_step_bf16(*args, f, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    for bad_scale in (float("inf"), float("nan"), 0.0, -1.0):
+        assert L.ringattn_step_bf16(P, P, P, P, P, ctypes.c_float(bad_scale), ctypes.byref(s), None) == \
+            _lib.RINGATTN_EINVAL
+    assert L.ringattn_step_bf16(P, P, P, P, P, f, ctypes.byref(shape(D=96)), None) == _lib.RINGATTN_EUNSUPPORTED
+    assert L.ringattn_step_bf16(P, P, P, P, P, f, None, None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_step_bf16(P, None, None, P, P, f, ctypes.byref(shape(Skv=0)), None) == 0
+    assert L.ringattn_acc_init_bf16(None, P, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_acc_init_bf16(P, None, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_acc_init_bf16(P, P, ctypes.byref(shape(Sq=0)), None) == _lib.RINGATTN_EINVAL
+    assert L.ringattn_acc_init_bf16(P, P, ctypes.byref(shape(D=80)), None) == _lib.RINGATTN_EUNSUPPORTED
