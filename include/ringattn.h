@@ -14,9 +14,10 @@
  *     kept in float32 for the merge; default True, the only mode built here),
  *     rotate_method "allgather" (every chunk is resident before the loop),
  *     ring_anything (any sequence length; uneven chunks).
- *   - Same guide, section "Ring Anything Attention": local K/V padded to the
- *     longest local length, all-gathered, and cut back to each block's true
- *     length before attention; inference only, no attention mask.
+ *   - Same guide, section "Ring Anything Attention" (uneven chunk lengths,
+ *     inference only, no attention mask): here chunk c is either a row range
+ *     of a packed K/V buffer or starts at row c * kv_chunk_stride of a
+ *     padded one; keys at or past its true length are masked and never read.
  *   - Same guide, section "Perhatian Ulysses": after the all-to-all each GPU
  *     holds every token for a subset of heads; its share is full-sequence
  *     attention over those heads (ringattn_forward with one chunk).

@@ -5,10 +5,10 @@ degree (context-parallelism guide, "Paralelisme konteks", diffusers v0.43.0,
 variant table: requirement of Ring Attention; the benchmark tables of the same
 page report ring as failing at 1008x1008, where the length does not divide).
 
-Ring Anything: any sequence length is accepted.  Each rank pads its local K/V
-to the longest local length, the padded blocks are all-gathered, and each
-block is cut back to its true length before attention (same guide, section
-"Ring Anything Attention"; Parallelism API page,
+Ring Anything: any sequence length is accepted.  The local K/V blocks differ
+in length; they travel in one buffer whose blocks all have the longest local
+length, and only the true rows of each block take part in attention (same
+guide, section "Ring Anything Attention"; Parallelism API page,
 ``ContextParallelConfig.ring_anything``).  The pages do not say which ranks
 get the longer chunks; the reading taken here is that the first ``S mod N``
 chunks hold one extra token, so lengths differ by at most one and the padded
