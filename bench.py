@@ -96,42 +96,94 @@ def traffic_from_profiles(workload: str, block_m: int):
         return None
 
 
-def cpu_baseline(x, target_s: float, q_key: str = "q"):
-    """Time the oracle on a sample of query rows of x[q_key] (all heads, all keys)."""
+# Inputs the oracle workers read: set in the parent before the pool forks, so
+# every worker inherits them copy-on-write instead of receiving them pickled.
+_ORACLE_INPUTS = {}
+
+
+def _oracle_worker_init():
+    """One BLAS thread per worker process: the pool supplies the parallelism."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # threadpoolctl missing: BLAS keeps its own count
+        pass
+
+
+def _oracle_task(task):
+    """The oracle on query rows `rows` of head h (all keys), in its own process."""
     import numpy as np
 
     import oracle
-    from context_attention_diffusion_ringattn_amd import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing or no BLAS info
-        threads = 1
+    h, rows = task
+    x = _ORACLE_INPUTS
+    q = x["q"][:, rows, h:h + 1, :].astype(np.float64)
+    k = x["k"][:, :, h:h + 1, :].astype(np.float64)
+    v = x["v"][:, :, h:h + 1, :].astype(np.float64)
+    out, lse = oracle.attention_fp64(q, k, v, x["scale"])
+    return h, rows, out, lse
+
+
+def oracle_workers() -> int:
+    """Worker processes for the oracle: the host cores this process may run
+    on, at most 16 (a GPU machine's CPU share per GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def make_oracle_pool(x, q_key: str = "q"):
+    """Fork the oracle's worker pool.  Called before the GPU is touched, so
+    the workers are plain CPU processes holding the bf16 inputs as float32."""
+    import multiprocessing as mp
+
+    _ORACLE_INPUTS.clear()
+    _ORACLE_INPUTS.update(q=x[q_key].float().numpy(), k=x["k"].float().numpy(), v=x["v"].float().numpy(),
+                          scale=x["scale"])
+    n = oracle_workers()
+    return mp.get_context("fork").Pool(n, initializer=_oracle_worker_init), n
+
+
+def cpu_baseline(x, target_s: float, pool, n_workers: int, q_key: str = "q"):
+    """Time the oracle on a sample of query rows of x[q_key] (all heads, all
+    keys), spread over the worker pool as (head, row block) tasks."""
+    import numpy as np
+
     w = x["workload"]
-    q64, k64, v64 = W.to_f64(x[q_key]), W.to_f64(x["k"]), W.to_f64(x["v"])
-    n_rows = q64.shape[1]
+    n_rows = x[q_key].shape[1]
     rng = np.random.default_rng(1234)
 
     def run(n):
         rows = sorted(int(r) for r in rng.choice(n_rows, size=min(n, n_rows), replace=False))
+        blk = max(1, -(-len(rows) * w.heads // (4 * n_workers)))  # about four tasks per worker
+        blk = min(blk, 256)
+        tasks = [(h, rows[i:i + blk]) for h in range(w.heads) for i in range(0, len(rows), blk)]
+        out = np.zeros((w.batch, len(rows), w.heads, w.head_dim))
+        lse = np.zeros((w.batch, w.heads, len(rows)))
+        pos = {r: i for i, r in enumerate(rows)}
         t0 = time.perf_counter()
-        out, lse = oracle.attention_rows_fp64(q64, k64, v64, x["scale"], rows)
+        for h, rr, o, l in pool.imap_unordered(_oracle_task, tasks):
+            idx = [pos[r] for r in rr]
+            out[:, idx, h, :] = o[:, :, 0, :]
+            lse[:, h, idx] = l[:, 0, :]
         return rows, out, lse, time.perf_counter() - t0
 
-    run(min(2, n_rows))                        # BLAS thread pool start-up, page faults
-    n0 = min(64, n_rows)
+    run(min(n_workers, n_rows))                 # worker start-up, page faults
+    n0 = min(4 * n_workers, n_rows)
     _, _, _, t0 = run(n0)
+    while t0 < target_s / 8 and n0 < n_rows:    # calibrate on a sample long enough to time
+        n0 = min(n_rows, 4 * n0)
+        _, _, _, t0 = run(n0)
     n = int(max(n0, min(n_rows, n0 * target_s / max(t0, 1e-3))))
     rows, out, lse, t = run(n)
     flops = 4.0 * w.batch * len(rows) * w.seq_len * w.head_dim * w.heads
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(n_workers),
         "kind": "oracle",
         "sample": f"{len(rows)} of {n_rows} query rows x {w.heads} heads x {w.seq_len} keys "
-                  f"(fp64 NumPy, {t:.1f} s)",
+                  f"(fp64 NumPy, {t:.1f} s wall on {n_workers} worker processes with one BLAS thread each; "
+                  f"{len(os.sched_getaffinity(0))} host cores in this process's affinity)",
     }, rows, out, lse
 
 
@@ -152,13 +204,18 @@ def main():
     import context_attention_diffusion_ringattn_amd as ra
     from context_attention_diffusion_ringattn_amd import workloads as W
 
-    if not torch.cuda.is_available():
+    # device_count() does not initialise the GPU (is_available() does), so the
+    # oracle's pool below is still forked from a process with no GPU state.
+    if torch.cuda.device_count() < 1:
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
-    dev = torch.device("cuda:0")
     x = W.make_inputs(args.workload)
     w = x["workload"]
     q_key = "q_full" if args.sweep else "q"
+    pool = None
+    if not args.no_cpu_baseline:
+        pool, n_workers = make_oracle_pool(x, q_key)   # forked before any GPU call
+    dev = torch.device("cuda:0")
     q, k, v = x[q_key].to(dev), x["k"].to(dev), x["v"].to(dev)
     n_q = q.shape[1]
     offs = ra.chunk_offsets(w.seq_len, w.n_chunks, w.ring_anything)
@@ -250,7 +307,9 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        cb, rows, ref_out, ref_lse = cpu_baseline(x, args.cpu_seconds, q_key)
+        cb, rows, ref_out, ref_lse = cpu_baseline(x, args.cpu_seconds, pool, n_workers, q_key)
+        pool.close()
+        pool.join()
         result["cpu_baseline"] = cb
         o = out[:, rows].detach().cpu().double().numpy()
         l = lse[:, :, rows].detach().cpu().double().numpy()

@@ -85,3 +85,20 @@ def test_inputs_are_seeded_and_local_shard_is_rank0():
     assert np.all(norms[a["k_outlier_rows"]] > 4.0)
     c = W.make_inputs("flux")
     assert not torch.equal(c["k"][:, :577], a["k"][:, :577])
+
+
+def test_cpu_baseline_pool_matches_oracle():
+    """The oracle timed over the worker pool gives the same rows as one call
+    of the oracle, and reports the worker count as its cores."""
+    import oracle
+    x = W.make_inputs("tiny")
+    pool, n = bench.make_oracle_pool(x)
+    try:
+        cb, rows, out, lse = bench.cpu_baseline(x, 0.2, pool, n)
+    finally:
+        pool.close()
+        pool.join()
+    assert cb["kind"] == "oracle" and cb["cores"] == n == bench.oracle_workers() and cb["value"] > 0
+    ref_out, ref_lse = oracle.attention_rows_fp64(W.to_f64(x["q"]), W.to_f64(x["k"]), W.to_f64(x["v"]),
+                                                  x["scale"], rows)
+    assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse)
