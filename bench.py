@@ -50,6 +50,9 @@ def parse_args():
     ap.add_argument("--sweep", action="store_true",
                     help="time the whole ring on this GPU instead of one shard: every rank's query rows, each "
                          "rank visiting the chunks in its rotated order with a float32 merge per step")
+    ap.add_argument("--ring-steps", action="store_true",
+                    help="time the ring's own loop on this shard instead of one forward call: accumulator "
+                         "initialisation plus one split ring step (ringattn_step_split, library plan) per chunk")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the HBM byte "
                          "counters of a profiler run) and exit")
@@ -229,9 +232,22 @@ def main():
 
         def step():
             ra.ring_sweep(q, k, v, chunk_offsets=offs, scale=x["scale"], out=out, lse=lse)
+    elif args.ring_steps:
+        # every chunk's step with the library's plan for its length; one workspace fits the largest
+        plans = [ra.step_plan(tuple(q.shape), offs[c + 1] - offs[c], args.splits, args.block_m)
+                 for c in range(w.n_chunks)]
+        ws = ra.new_workspace(max(p[2] for p in plans), dev)
+        n_splits, block_m = plans[0][0], plans[0][1]
+        chunks = [(k[:, offs[c]:offs[c + 1]], v[:, offs[c]:offs[c + 1]]) for c in range(w.n_chunks)]
+        assert all(kc.is_contiguous() for kc, _ in chunks), "chunk views must be contiguous (batch 1)"
+
+        def step():
+            ra.acc_init(out, lse)
+            for (kc, vc), (sp, bm, _) in zip(chunks, plans):
+                ra.step(q, kc, vc, out, lse, scale=x["scale"], n_splits=sp, block_m=bm, workspace=ws)
     else:
         n_splits, block_m, ws_bytes = ra.forward_plan(tuple(q.shape), offs, args.splits, args.block_m)
-        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+        ws = ra.new_workspace(ws_bytes, dev)
 
         def step():
             ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=n_splits, block_m=block_m,
@@ -269,7 +285,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
 
-    traffic = None if args.sweep else traffic_from_profiles(args.workload, block_m)
+    traffic = None if (args.sweep or args.ring_steps) else traffic_from_profiles(args.workload, block_m)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -284,9 +300,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}_ring_sweep" if args.sweep else w.name,
+            "workload": f"{w.name}_ring_sweep" if args.sweep else (f"{w.name}_ring_steps" if args.ring_steps
+                                                                    else w.name),
             "description": (f"every rank of the ring on one GPU ({w.n_chunks} ranks, rank-rotated chunk order, "
-                            f"float32 merge per step); " if args.sweep else "") + w.description,
+                            f"float32 merge per step); " if args.sweep else "")
+                           + (f"the ring's loop: accumulator init + {w.n_chunks} split ring steps; "
+                              if args.ring_steps else "") + w.description,
             "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
             "q_rows": n_q, "kv_rows": w.seq_len, "n_chunks": w.n_chunks,
             "ring_anything": w.ring_anything,

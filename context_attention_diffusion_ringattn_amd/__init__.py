@@ -17,6 +17,8 @@ from .ringattn import (
     merge,
     new_accumulators,
     new_accumulators_bf16,
+    new_workspace,
+    step_plan,
     ring_shard,
     ring_sweep,
     step,
@@ -36,6 +38,8 @@ __all__ = [
     "merge",
     "new_accumulators",
     "new_accumulators_bf16",
+    "new_workspace",
+    "step_plan",
     "ring_shard",
     "ring_sweep",
     "step",

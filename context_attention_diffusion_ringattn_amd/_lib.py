@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "ringattn_cp_layout",
     "ringattn_acc_init_bf16",
     "ringattn_step_bf16",
+    "ringattn_step_split",
 )
 
 
@@ -118,6 +119,7 @@ _SIGNATURES = {
     "ringattn_cp_layout": (ctypes.c_int, [ctypes.POINTER(CpConfig), _i32, ctypes.POINTER(CpShare)]),
     "ringattn_acc_init_bf16": (ctypes.c_int, [_vp, _vp, _shape_p, _vp]),
     "ringattn_step_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _shape_p, _vp]),
+    "ringattn_step_split": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _shape_p, _plan_p, _vp, _sz, _vp]),
 }
 
 

@@ -9,6 +9,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
+#include <cstdint>
 #include <mutex>
 #include <string>
 
@@ -20,7 +22,7 @@ using namespace ringattn;
 
 static_assert(kMaxChunks == RINGATTN_MAX_CHUNKS, "chunk limit mismatch");
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 
 thread_local std::string g_last_error;
 
@@ -158,19 +160,39 @@ struct Plan {
     size_t ws_bytes;
     int64_t split_out_stride;
     int64_t split_lse_stride;
+    size_t lse_off;    // byte offset of the split LSE slots in the workspace
 };
+
+size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Workspace of a K/V-split plan: n_splits float32 output slots, then
+// n_splits float32 LSE slots (16-byte aligned).  No workspace without splits.
+void plan_workspace(const ringattn_shape *s, Plan *p) {
+    p->split_out_stride = (int64_t)s->batch * s->q_len * s->heads * s->head_dim;
+    p->split_lse_stride = (int64_t)s->batch * s->heads * s->q_len;
+    if (p->n_splits <= 1) {
+        p->ws_bytes = p->lse_off = 0;
+        return;
+    }
+    p->lse_off = align16((size_t)p->n_splits * (size_t)p->split_out_stride * 4u);
+    p->ws_bytes = align16(p->lse_off + (size_t)p->n_splits * (size_t)p->split_lse_stride * 4u);
+}
 
 // Cost model of one launch, in microseconds.  Workgroups run in rounds of
 // `slots` (one 8-wave workgroup or three 4-wave workgroups per CU); a
-// workgroup costs its tile count times the time one tile takes when every
-// CU is busy (64-key tiles for the 8-wave kernel, 32-key tiles for the
-// 4-wave one), plus a fixed start/finish cost; K/V splits add the float32
-// partial traffic (written once, read once by the merge) at HBM speed.  The
-// constants are measured on MI355X (video-sized shards).
+// workgroup costs its tile count times the time one tile takes (64-key
+// tiles for the 8-wave kernel, 32-key tiles for the 4-wave one), plus a
+// fixed start/finish cost; K/V splits add the float32 partial traffic
+// (written once, read once by the merge) at HBM speed and the merge
+// launch.  A 4-wave workgroup's tile time grows with the number of
+// workgroups sharing its CU (1.47 us with three).  The constants are
+// measured on MI355X.
 double plan_cost(const ringattn_shape *s, int32_t n_tiles, int block_m, int splits) {
     const double cus = cu_count_for_current_device();
     const double slots = block_m == 256 ? cus : 3.0 * cus;
-    const double tile_us = block_m == 256 ? 1.79 : 1.47;
+    const double n_wg = std::ceil((double)s->q_len / block_m) * s->heads * s->batch * splits;
+    const double per_cu = std::min(3.0, std::ceil(n_wg / cus));
+    const double tile_us = block_m == 256 ? 1.79 : 1.47 * (0.4 + 0.6 * per_cu / 3.0);
     const double fixed_us = 3.0;
     const double n_qtiles = std::ceil((double)s->q_len / block_m);
     const double base = n_qtiles * s->heads * s->batch;
@@ -184,13 +206,19 @@ double plan_cost(const ringattn_shape *s, int32_t n_tiles, int block_m, int spli
     return cost;
 }
 
-int make_plan(const ringattn_shape *s, const Layout &L, int32_t req_splits, int32_t req_block_m, Plan *p) {
+// Choose (or check) a launch plan.  req_*: the caller's requests (0 =
+// choose).  max_ws: the largest workspace the caller can offer
+// (SIZE_MAX = any); plans that need more are not chosen, and a requested
+// split count whose workspace exceeds it is an error.
+int make_plan(const ringattn_shape *s, const Layout &L, int32_t req_splits, int32_t req_block_m, Plan *p,
+              size_t max_ws = SIZE_MAX) {
     if (req_splits < 0) return fail(RINGATTN_EINVAL, "requested n_splits must be >= 0");
     if (req_block_m != 0 && req_block_m != 128 && req_block_m != 256)
         return fail(RINGATTN_EINVAL, "block_m must be 0 (choose), 128 or 256 (got %d)", req_block_m);
     double best = 1e300;
     p->block_m = 0;
     p->n_splits = 1;
+    size_t need_min = SIZE_MAX;
     for (int bm : {256, 128}) {
         if (req_block_m != 0 && bm != req_block_m) continue;
         const int32_t n_tiles = bm == 256 ? L.ct.n_tiles : L.ct32.n_tiles;
@@ -198,6 +226,15 @@ int make_plan(const ringattn_shape *s, const Layout &L, int32_t req_splits, int3
         const int lo = req_splits > 0 ? (req_splits < cap ? req_splits : cap) : 1;
         const int hi = req_splits > 0 ? lo : cap;
         for (int sp = lo; sp <= hi; ++sp) {
+            Plan cand;
+            cand.block_m = bm;
+            cand.n_splits = sp;
+            cand.n_qtiles = (int32_t)std::min<int64_t>((s->q_len + bm - 1) / bm, INT32_MAX);
+            plan_workspace(s, &cand);
+            if (cand.ws_bytes > max_ws) {
+                need_min = std::min(need_min, cand.ws_bytes);
+                continue;
+            }
             const double c = plan_cost(s, n_tiles, bm, sp);
             if (c < best * 0.999) {
                 best = c;
@@ -206,17 +243,15 @@ int make_plan(const ringattn_shape *s, const Layout &L, int32_t req_splits, int3
             }
         }
     }
+    if (p->block_m == 0)
+        return fail(RINGATTN_EWORKSPACE, "the requested plan needs %zu workspace bytes, more than the %zu available",
+                    need_min, max_ws);
     const int64_t n_qtiles = (s->q_len + p->block_m - 1) / p->block_m;
     if (n_qtiles > INT32_MAX) return fail(RINGATTN_EINVAL, "q_len too large");
     p->n_qtiles = (int32_t)n_qtiles;
     const int64_t grid = n_qtiles * s->heads * s->batch * (int64_t)p->n_splits;
     if (grid > INT32_MAX) return fail(RINGATTN_EINVAL, "grid too large (%lld workgroups)", (long long)grid);
-    p->split_out_stride = (int64_t)s->batch * s->q_len * s->heads * s->head_dim;
-    p->split_lse_stride = (int64_t)s->batch * s->heads * s->q_len;
-    p->ws_bytes = p->n_splits > 1 ? (size_t)p->n_splits * (size_t)(p->split_out_stride + p->split_lse_stride) * 4u
-                                  : 0u;
-    // keep the lse slots 16-byte aligned after the out slots
-    if (p->n_splits > 1) p->ws_bytes += 16;
+    plan_workspace(s, p);
     return RINGATTN_OK;
 }
 
@@ -244,6 +279,86 @@ void fill_common(AttnArgs *a, const uint16_t *q, const uint16_t *k, const uint16
     a->heads = s->heads;
     a->scale = scale;
     a->scale_log2e = (float)((double)scale * 1.4426950408889634);
+}
+
+// Launch a planned attention pass over the layout L.  accum = 0: write the
+// result to out / lse; accum = 1: LSE-merge it into the float32 accumulator
+// out / lse in place (a ring step).  With more than one split the attention
+// kernel writes the splits' partials to the workspace and a merge kernel
+// combines them into out / lse.
+int run_planned(const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse, float scale,
+                const ringattn_shape *shape, const Layout &L, const Plan &p, void *workspace, bool accum,
+                hipStream_t s) {
+    AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    fill_common(&a, q, k, v, out, lse, scale, shape);
+    a.ct = L.ct;
+    a.kv_rows = L.kv_rows;
+    a.n_qtiles = p.n_qtiles;
+    a.n_splits = p.n_splits;
+    if (p.n_splits == 1)
+        return check_hip(launch_plan(a, p, L, shape->head_dim, accum ? kModeAccum : kModeFinal, s),
+                         "attention launch");
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    float *part_out = reinterpret_cast<float *>(ws);
+    float *part_lse = reinterpret_cast<float *>(ws + p.lse_off);
+    a.out = part_out;
+    a.lse = part_lse;
+    a.split_out_stride = p.split_out_stride;
+    a.split_lse_stride = p.split_lse_stride;
+    int st;
+    if ((st = check_hip(launch_plan(a, p, L, shape->head_dim, kModePartial, s), "attention launch"))) return st;
+    MergeSplitsArgs m;
+    m.part_out = part_out;
+    m.part_lse = part_lse;
+    m.out = out;
+    m.lse = lse;
+    m.q_len = shape->q_len;
+    m.batch = shape->batch;
+    m.heads = shape->heads;
+    m.n_splits = p.n_splits;
+    m.split_out_stride = p.split_out_stride;
+    m.split_lse_stride = p.split_lse_stride;
+    m.accum = accum ? 1 : 0;
+    return check_hip(launch_merge_splits(m, shape->head_dim, s), "split merge launch");
+}
+
+
+int check_workspace(const Plan &p, void *workspace, size_t workspace_bytes) {
+    if (p.n_splits <= 1) return RINGATTN_OK;
+    if (!workspace || workspace_bytes < p.ws_bytes)
+        return fail(RINGATTN_EWORKSPACE, "plan with %d splits needs %zu workspace bytes, got %zu", p.n_splits,
+                    p.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(RINGATTN_EINVAL, "workspace is not 16-byte aligned");
+    return RINGATTN_OK;
+}
+
+// ringattn_forward with the plan restricted to workspaces of at most max_ws bytes.
+int forward_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
+                 int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
+                 const ringattn_shape *shape, const ringattn_plan *plan, void *workspace, size_t workspace_bytes,
+                 size_t max_ws, hipStream_t s) {
+    int st;
+    if ((st = check_shape(shape, true))) return st;
+    if ((st = check_ptr(q, 16, "q"))) return st;
+    if ((st = check_ptr(out, 16, "out"))) return st;
+    if ((st = check_ptr(lse, 4, "lse"))) return st;
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(RINGATTN_EINVAL, "scale must be finite and > 0");
+    Layout L;
+    if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
+    Plan p;
+    if ((st = make_plan(shape, L, plan ? plan->n_splits : 0, plan ? plan->block_m : 0, &p, max_ws))) return st;
+    if (L.ct.n_tiles > 0) {
+        if ((st = check_ptr(k, 16, "k"))) return st;
+        if ((st = check_ptr(v, 16, "v"))) return st;
+    }
+    if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+    if (L.ct.n_tiles == 0) {  // no keys at all: the empty result
+        const int64_t n_out = (int64_t)shape->batch * shape->q_len * shape->heads * shape->head_dim;
+        const int64_t n_lse = (int64_t)shape->batch * shape->heads * shape->q_len;
+        return check_hip(launch_acc_init(out, lse, n_out, n_lse, s), "acc_init launch");
+    }
+    return run_planned(q, k, v, out, lse, scale, shape, L, p, workspace, false, s);
 }
 
 }  // namespace
@@ -298,29 +413,30 @@ int ringattn_acc_init(float *out_acc, float *lse_acc, const ringattn_shape *shap
 
 int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk, float *out_acc,
                   float *lse_acc, float scale, const ringattn_shape *shape, void *stream) {
+    const ringattn_plan one = {1, 0, 0};
+    return ringattn_step_split(q, k_chunk, v_chunk, out_acc, lse_acc, scale, shape, &one, nullptr, 0, stream);
+}
+
+int ringattn_step_split(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk, float *out_acc,
+                        float *lse_acc, float scale, const ringattn_shape *shape, const ringattn_plan *plan,
+                        void *workspace, size_t workspace_bytes, void *stream) {
     int st;
     if ((st = check_shape(shape, true))) return st;
     if ((st = check_ptr(q, 16, "q"))) return st;
     if ((st = check_ptr(out_acc, 16, "out_acc"))) return st;
     if ((st = check_ptr(lse_acc, 4, "lse_acc"))) return st;
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(RINGATTN_EINVAL, "scale must be finite and > 0");
-    if (shape->kv_len == 0) return ok();  // an empty chunk is the merge identity
-    if ((st = check_ptr(k_chunk, 16, "k_chunk"))) return st;
-    if ((st = check_ptr(v_chunk, 16, "v_chunk"))) return st;
-    AttnArgs a;
-    std::memset(&a, 0, sizeof a);
     Layout L;
     const int64_t offs[2] = {0, shape->kv_len};
     if ((st = build_layout(offs, 1, 0, shape->kv_len, &L))) return st;
     Plan p;
-    if ((st = make_plan(shape, L, 1, 0, &p))) return st;
-    fill_common(&a, q, k_chunk, v_chunk, out_acc, lse_acc, scale, shape);
-    a.ct = L.ct;
-    a.kv_rows = L.kv_rows;
-    a.n_qtiles = p.n_qtiles;
-    a.n_splits = 1;
-    return check_hip(launch_plan(a, p, L, shape->head_dim, kModeAccum, (hipStream_t)stream),
-                     "attention launch");
+    if ((st = make_plan(shape, L, plan ? plan->n_splits : 0, plan ? plan->block_m : 0, &p))) return st;
+    if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
+    if (shape->kv_len == 0) return ok();  // an empty chunk is the merge identity
+    if ((st = check_ptr(k_chunk, 16, "k_chunk"))) return st;
+    if ((st = check_ptr(v_chunk, 16, "v_chunk"))) return st;
+    return run_planned(q, k_chunk, v_chunk, out_acc, lse_acc, scale, shape, L, p, workspace, true,
+                       (hipStream_t)stream);
 }
 
 int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
@@ -355,64 +471,8 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
                      int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
                      const ringattn_shape *shape, const ringattn_plan *plan, void *workspace, size_t workspace_bytes,
                      void *stream) {
-    int st;
-    if ((st = check_shape(shape, true))) return st;
-    if ((st = check_ptr(q, 16, "q"))) return st;
-    if ((st = check_ptr(out, 16, "out"))) return st;
-    if ((st = check_ptr(lse, 4, "lse"))) return st;
-    if (!(std::isfinite(scale) && scale > 0.f)) return fail(RINGATTN_EINVAL, "scale must be finite and > 0");
-    AttnArgs a;
-    std::memset(&a, 0, sizeof a);
-    Layout L;
-    if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
-    Plan p;
-    if ((st = make_plan(shape, L, plan ? plan->n_splits : 0, plan ? plan->block_m : 0, &p))) return st;
-    a.ct = L.ct;
-    if (a.ct.n_tiles > 0) {
-        if ((st = check_ptr(k, 16, "k"))) return st;
-        if ((st = check_ptr(v, 16, "v"))) return st;
-    }
-    if (p.n_splits > 1) {
-        if (!workspace || workspace_bytes < p.ws_bytes)
-            return fail(RINGATTN_EWORKSPACE, "plan with %d splits needs %zu workspace bytes, got %zu", p.n_splits,
-                        p.ws_bytes, workspace ? workspace_bytes : (size_t)0);
-        if (!aligned(workspace, 16)) return fail(RINGATTN_EINVAL, "workspace is not 16-byte aligned");
-    }
-    hipStream_t s = (hipStream_t)stream;
-    if (a.ct.n_tiles == 0) {  // no keys at all: the empty result
-        const int64_t n_out = (int64_t)shape->batch * shape->q_len * shape->heads * shape->head_dim;
-        const int64_t n_lse = (int64_t)shape->batch * shape->heads * shape->q_len;
-        return check_hip(launch_acc_init(out, lse, n_out, n_lse, s), "acc_init launch");
-    }
-    fill_common(&a, q, k, v, out, lse, scale, shape);
-    a.kv_rows = L.kv_rows;
-    a.n_qtiles = p.n_qtiles;
-    a.n_splits = p.n_splits;
-    if (p.n_splits == 1)
-        return check_hip(launch_plan(a, p, L, shape->head_dim, kModeFinal, s), "attention launch");
-
-    float *part_out = static_cast<float *>(workspace);
-    uintptr_t lse_addr = reinterpret_cast<uintptr_t>(part_out + (size_t)p.n_splits * p.split_out_stride);
-    lse_addr = (lse_addr + 15) & ~(uintptr_t)15;
-    float *part_lse = reinterpret_cast<float *>(lse_addr);
-    a.out = part_out;
-    a.lse = part_lse;
-    a.split_out_stride = p.split_out_stride;
-    a.split_lse_stride = p.split_lse_stride;
-    if ((st = check_hip(launch_plan(a, p, L, shape->head_dim, kModePartial, s), "attention launch")))
-        return st;
-    MergeSplitsArgs m;
-    m.part_out = part_out;
-    m.part_lse = part_lse;
-    m.out = out;
-    m.lse = lse;
-    m.q_len = shape->q_len;
-    m.batch = shape->batch;
-    m.heads = shape->heads;
-    m.n_splits = p.n_splits;
-    m.split_out_stride = p.split_out_stride;
-    m.split_lse_stride = p.split_lse_stride;
-    return check_hip(launch_merge_splits(m, shape->head_dim, s), "split merge launch");
+    return forward_impl(q, k, v, chunk_offsets, n_chunks, kv_chunk_stride, out, lse, scale, shape, plan, workspace,
+                        workspace_bytes, SIZE_MAX, (hipStream_t)stream);
 }
 
 int ringattn_ring_sweep(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,

@@ -70,6 +70,7 @@ struct MergeSplitsArgs {
     int32_t n_splits;
     int64_t split_out_stride;
     int64_t split_lse_stride;
+    int32_t accum;  // 0: write the merged result to out / lse; 1: LSE-merge it into them in place
 };
 
 // 4-wave, 128-row variant (three workgroups per CU, 32-key tiles; the chunk

@@ -16,13 +16,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMergeThreads = 256;
 
-// out/lse <- merge over n_splits partial slots.  A workgroup owns kMergeSlice
-// consecutive 16-byte pieces of the output (a contiguous range of every
-// partial slot and of out, covering kMergeSlice / (D/4) whole (b, i, h)
-// rows).  One thread per row first reads the row's split LSEs, writes the
-// merged LSE and leaves the split weights exp(l_s - lse) in LDS (0 for an
-// empty split, whose slot is then never read); then every thread merges its
-// pieces.
+// out/lse <- merge over n_splits partial slots (accum = 0), or
+// out/lse <- merge(out/lse, merge over the slots) in place (accum = 1: the
+// split ring step's float32 accumulator; where its lse is -inf it is
+// replaced, never multiplied).  A workgroup owns kMergeSlice consecutive
+// 16-byte pieces of the output (a contiguous range of every partial slot and
+// of out, covering kMergeSlice / (D/4) whole (b, i, h) rows).  One thread per
+// row first reads the row's split LSEs, writes the merged LSE and leaves the
+// weights in LDS -- exp(l_s - lse) per split (0 for an empty split, whose
+// slot is then never read) and the accumulator's own weight; then every
+// thread merges its pieces.
 constexpr int kMergePer = 2;
 constexpr int kMergeSlice = kMergeThreads * kMergePer;
 
@@ -30,7 +33,8 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_slice_kernel(const MergeSplitsArgs a) {
     constexpr int G = D / 4;
     constexpr int NP = kMergeSlice / G;  // rows per workgroup
-    __shared__ float w[NP * kMaxSplits];
+    constexpr int WS = kMaxSplits + 1;  // per row: the splits, then the accumulator
+    __shared__ float w[NP * WS];
     const int NS = a.n_splits;
     const int64_t n4 = (int64_t)a.batch * a.q_len * a.heads * G;
     const int64_t e0 = (int64_t)blockIdx.x * kMergeSlice;
@@ -54,11 +58,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_slice_kernel(const MergeS
             }
             lse = mx + logf(sum);
         }
+        float wb = 1.f, wa = 0.f, lse_out = lse;
+        if (a.accum) {
+            const float la = a.lse[lse_idx];
+            if (lse == -INFINITY) {  // no keys in any split: the accumulator is unchanged
+                wa = 1.f;
+                lse_out = la;
+            } else if (la != -INFINITY) {
+                lse_out = fmaxf(la, lse) + log1pf(expf(-fabsf(la - lse)));
+                wa = expf(la - lse_out);
+                wb = expf(lse - lse_out);
+            }
+        }
         for (int sp = 0; sp < NS; ++sp) {
             const float l = lp[sp * a.split_lse_stride];
-            w[threadIdx.x * kMaxSplits + sp] = (lse == -INFINITY || l == -INFINITY) ? 0.f : expf(l - lse);
+            w[threadIdx.x * WS + sp] = (lse == -INFINITY || l == -INFINITY) ? 0.f : wb * expf(l - lse);
         }
-        a.lse[lse_idx] = lse;
+        w[threadIdx.x * WS + kMaxSplits] = wa;
+        a.lse[lse_idx] = lse_out;
     }
     __syncthreads();
     const f32x4 *part = (const f32x4 *)a.part_out;
@@ -68,12 +85,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_slice_kernel(const MergeS
         const int le = k * kMergeThreads + threadIdx.x;
         const int64_t e = e0 + le;
         if (e >= n4) break;
-        const float *we = w + (le / G) * kMaxSplits;
+        const float *we = w + (le / G) * WS;
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < NS; ++sp) {
             const float ws = we[sp];
             if (ws != 0.f) acc += ws * part[sp * stride4 + e];
         }
+        const float wa = we[kMaxSplits];
+        if (wa != 0.f) acc += wa * ((const f32x4 *)a.out)[e];
         ((f32x4 *)a.out)[e] = acc;
     }
 }

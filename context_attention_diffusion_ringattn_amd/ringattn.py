@@ -158,10 +158,39 @@ def new_accumulators(q: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.
     return out, lse
 
 
+def new_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """A split workspace of ``nbytes`` bytes (None when no workspace is
+    needed); its contents on entry do not matter."""
+    if not nbytes:
+        return None
+    return torch.empty((int(nbytes),), dtype=torch.uint8, device=device)
+
+
+def _workspace_args(workspace: Optional[torch.Tensor], device):
+    if workspace is None:
+        return _ptr(None), 0
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    _check_device(workspace, "workspace", device)
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def step_plan(q_shape: Sequence[int], kv_len: int, n_splits: int = 0, block_m: int = 0) -> Tuple[int, int, int]:
+    """(n_splits, block_m, workspace_bytes) of the plan of a split ring step
+    over a chunk of kv_len keys (the plan of a one-chunk forward)."""
+    return forward_plan(q_shape, [0, int(kv_len)], n_splits, block_m)
+
+
 def step(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out_acc: torch.Tensor,
-         lse_acc: torch.Tensor, scale: Optional[float] = None, stream=None) -> None:
+         lse_acc: torch.Tensor, scale: Optional[float] = None, stream=None, *, n_splits: int = 1,
+         block_m: int = 0, workspace: Optional[torch.Tensor] = None) -> None:
     """One ring step: attend q to one K/V chunk and LSE-merge into the float32
-    accumulators in place (the merge is fused into the kernel epilogue)."""
+    accumulators in place (the merge is fused into the kernel epilogue).
+
+    ``n_splits`` = 1 (default): ``ringattn_step``, one workgroup per query
+    tile over the whole chunk.  Otherwise ``ringattn_step_split`` with that
+    many key splits (0 = the library's plan); ``workspace`` as from
+    ``new_workspace(step_plan(...)[2])``, allocated here when not given."""
     _check_bf16(q, "q")
     _check_bf16(k_chunk, "k_chunk")
     _check_bf16(v_chunk, "v_chunk")
@@ -175,9 +204,18 @@ def step(q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor, out_acc:
     if scale is None:
         scale = default_scale(D)
     shape = _shape(q, k_chunk.shape[1])
-    check(lib().ringattn_step(_ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(out_acc), _ptr(lse_acc),
-                              ctypes.c_float(scale), ctypes.byref(shape), _stream_handle(q.device, stream)),
-          "ringattn_step")
+    if int(n_splits) == 1 and workspace is None and int(block_m) == 0:
+        check(lib().ringattn_step(_ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(out_acc), _ptr(lse_acc),
+                                  ctypes.c_float(scale), ctypes.byref(shape), _stream_handle(q.device, stream)),
+              "ringattn_step")
+        return
+    plan = Plan(n_splits=int(n_splits), block_m=int(block_m), workspace_bytes=0)
+    if workspace is None:
+        workspace = new_workspace(step_plan(q.shape, k_chunk.shape[1], n_splits, block_m)[2], q.device)
+    ws_ptr, ws_len = _workspace_args(workspace, q.device)
+    check(lib().ringattn_step_split(_ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(out_acc), _ptr(lse_acc),
+                                    ctypes.c_float(scale), ctypes.byref(shape), ctypes.byref(plan), ws_ptr, ws_len,
+                                    _stream_handle(q.device, stream)), "ringattn_step_split")
 
 
 def new_accumulators_bf16(q: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -303,14 +341,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     if workspace is None:
         check(lib().ringattn_forward_plan(ctypes.byref(shape), arr, n_chunks, int(kv_chunk_stride),
                                           ctypes.byref(plan)), "ringattn_forward_plan")
-        if plan.workspace_bytes:
-            workspace = torch.empty((plan.workspace_bytes,), dtype=torch.uint8, device=q.device)
-    if workspace is not None:
-        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor")
-        _check_device(workspace, "workspace", q.device)
-    ws_ptr = _ptr(workspace)
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = new_workspace(plan.workspace_bytes, q.device)
+    ws_ptr, ws_len = _workspace_args(workspace, q.device)
     check(lib().ringattn_forward(_ptr(q), _ptr(k), _ptr(v), arr, n_chunks, int(kv_chunk_stride), _ptr(out), _ptr(lse),
                                  ctypes.c_float(scale), ctypes.byref(shape), ctypes.byref(plan), ws_ptr, ws_len,
                                  _stream_handle(q.device, stream)), "ringattn_forward")

@@ -112,7 +112,9 @@ int ringattn_acc_init(float *out_acc, float *lse_acc, const ringattn_shape *shap
  * copied (the old accumulator output is never multiplied).  The merge is
  * fused into the attention kernel's epilogue.  kv_len = 0 is a no-op.
  * Start from ringattn_acc_init; after all N chunks the accumulators hold the
- * shard's attention output and LSE.  scale must be finite and > 0.
+ * shard's attention output and LSE.  scale must be finite and > 0.  One
+ * workgroup sweeps each query tile over the whole chunk (no workspace);
+ * ringattn_step_split below can spread the chunk's keys over several.
  */
 int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk,
                   float *out_acc, float *lse_acc, float scale,
@@ -130,11 +132,16 @@ int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const 
 /*
  * Launch plan of ringattn_forward.
  *   n_splits: number of key/value splits -- independent partial passes over
- *     disjoint ranges of K/V tiles, merged at the end by their LSE;
+ *     disjoint ranges of K/V tiles, merged by their LSE in split order by a
+ *     merge kernel that follows the attention kernel on the stream;
  *   block_m: query rows per workgroup, 128 (4 waves, three workgroups per
  *     compute unit, 32-key tiles) or 256 (8 waves in two groups that
  *     alternate MFMA and softmax phases, 64-key tiles);
- *   workspace_bytes: device workspace the plan needs (0 when n_splits is 1).
+ *   workspace_bytes: device workspace the plan needs (0 when n_splits is 1):
+ *     the float32 partial outputs of the splits, then their float32 LSEs
+ *     (16-byte aligned).  Its contents on entry do not matter; calls that
+ *     use one workspace must not overlap in time (same stream, or ordered by
+ *     the caller).
  * On input n_splits and block_m are requests (0 = the library chooses from
  * the shape and the GPU's compute-unit count; n_splits > 0 is clamped to the
  * K/V tile count of the chosen kernel); on output they hold what
@@ -145,6 +152,24 @@ typedef struct ringattn_plan {
     int32_t block_m;
     uint64_t workspace_bytes;
 } ringattn_plan;
+
+/*
+ * The ring step of ringattn_step (same arguments, same result, the same
+ * float32 LSE merge into out_acc / lse_acc) with a launch plan: the chunk's
+ * keys may be split over plan->n_splits workgroups per query tile, whose
+ * partials are merged by their LSE and then into the accumulator by a merge
+ * kernel enqueued after the attention kernel (context parallelism guide,
+ * section "Ring Attention":
+ * one attention pass per chunk, overlapped with the ring's communication;
+ * Parallelism API page, ContextParallelConfig.convert_to_fp32).  Plan it as
+ * a one-chunk ringattn_forward: ringattn_forward_plan(shape, {0, kv_len},
+ * 1, 0, &plan).  plan: NULL for the library's choice, else the requests of
+ * a ringattn_plan.  workspace: as for ringattn_forward.  kv_len = 0 is a
+ * no-op.
+ */
+int ringattn_step_split(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk,
+                        float *out_acc, float *lse_acc, float scale, const ringattn_shape *shape,
+                        const ringattn_plan *plan, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Fill *plan (see ringattn_plan) for a ringattn_forward call with these

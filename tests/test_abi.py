@@ -40,7 +40,7 @@ def test_header_symbols_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ringattn_abi_version() == 5
+    assert L.ringattn_abi_version() == 6
     assert _lib.status_string(0) == "RINGATTN_OK"
     assert _lib.status_string(-1) == "RINGATTN_EINVAL"
     assert _lib.status_string(-2) == "RINGATTN_EUNSUPPORTED"
@@ -288,3 +288,39 @@ def test_bf16_state_calls_validate(L):
     assert L.ringattn_acc_init_bf16(P, None, ctypes.byref(s), None) == _lib.RINGATTN_EINVAL
     assert L.ringattn_acc_init_bf16(P, P, ctypes.byref(shape(Sq=0)), None) == _lib.RINGATTN_EINVAL
     assert L.ringattn_acc_init_bf16(P, P, ctypes.byref(shape(D=80)), None) == _lib.RINGATTN_EUNSUPPORTED
+
+
+def _step_split(L, s, splits=0, block_m=0, ws=None, ws_bytes=0, q=P, k=P, v=P, out=P, lse=P, scale=0.125):
+    plan = _lib.Plan(n_splits=splits, block_m=block_m, workspace_bytes=0)
+    return L.ringattn_step_split(q, k, v, out, lse, ctypes.c_float(scale), ctypes.byref(s), ctypes.byref(plan), ws,
+                                 ws_bytes, None)
+
+
+def test_step_split_validation(L):
+    """The split ring step checks its plan and workspace like forward does,
+    before any launch; its workspace is the one-chunk forward plan's."""
+    s = shape(B=1, H=2, D=128, Sq=128, Skv=4096)
+    st, plan = _plan(L, s, [0, 4096], splits=4, block_m=256)
+    assert st == 0 and plan.n_splits == 4 and plan.workspace_bytes > 0
+    ws = plan.workspace_bytes
+    assert _step_split(L, s, splits=4, block_m=256) == _lib.RINGATTN_EWORKSPACE
+    assert _step_split(L, s, splits=4, block_m=256, ws=P, ws_bytes=ws - 1) == _lib.RINGATTN_EWORKSPACE
+    assert _step_split(L, s, splits=4, block_m=256, ws=P_MISALIGNED, ws_bytes=ws) == _lib.RINGATTN_EINVAL
+    assert _step_split(L, s, splits=4, block_m=100, ws=P, ws_bytes=ws) == _lib.RINGATTN_EINVAL
+    assert _step_split(L, s, splits=-1) == _lib.RINGATTN_EINVAL
+    assert _step_split(L, s, splits=1, block_m=256, q=None) == _lib.RINGATTN_EINVAL
+    assert _step_split(L, s, splits=1, block_m=256, scale=float("nan")) == _lib.RINGATTN_EINVAL
+    assert _step_split(L, shape(D=96, Sq=128, Skv=128), splits=1) == _lib.RINGATTN_EUNSUPPORTED
+    # an empty chunk is the merge identity: nothing to launch, no workspace needed
+    assert _step_split(L, shape(B=1, H=2, D=128, Sq=128, Skv=0), splits=4, k=None, v=None) == _lib.RINGATTN_OK
+
+
+def test_workspace_layout(L):
+    """A split plan's workspace holds the float32 output slots of every split,
+    then their LSE slots, 16-byte aligned -- nothing else."""
+    a16 = lambda x: (x + 15) // 16 * 16
+    for (B, H, D, Sq, Skv, splits, bm) in ((1, 24, 128, 577, 4611, 3, 256), (2, 3, 64, 300, 5000, 5, 128)):
+        st, plan = _plan(L, shape(B=B, H=H, D=D, Sq=Sq, Skv=Skv), [0, Skv], splits=splits, block_m=bm)
+        assert st == 0 and plan.n_splits == splits
+        lse_off = a16(splits * B * Sq * H * D * 4)
+        assert plan.workspace_bytes == a16(lse_off + splits * B * H * Sq * 4)

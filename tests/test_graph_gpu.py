@@ -46,7 +46,7 @@ def test_forward_with_split_in_a_graph(ra):
     offs = ra.chunk_offsets(w.seq_len, w.n_chunks, True)
     n_splits, block_m, ws_bytes = ra.forward_plan(tuple(q.shape), offs, 3, 256)
     assert n_splits == 3 and ws_bytes > 0
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws = ra.new_workspace(ws_bytes, dev)
     out = torch.empty((1, q.shape[1], w.heads, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((1, w.heads, q.shape[1]), dtype=torch.float32, device=dev)
 

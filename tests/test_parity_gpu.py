@@ -83,7 +83,7 @@ def test_forward_small_workloads(ra, name):
 @pytest.mark.parametrize("block_m", [128, 256])
 def test_forward_forced_splits(ra, name, splits, block_m):
     """Every split count and both workgroup shapes give the oracle's result
-    (the split partials are merged by LSE in the merge kernel)."""
+    (the last split of each query tile merges the partials by their LSE)."""
     x = workload_inputs(name)
     w = x["workload"]
     print(f"case {name} splits={splits} block_m={block_m}", flush=True)
