@@ -111,7 +111,8 @@ def test_sweep_small_full(ra, case):
 def test_sweep_rank_equals_its_shard(ra):
     """Each rank's rows of the sweep equal that rank's own shard computed alone
     (forward over the packed chunks in all-gather order) up to rounding, and
-    the step path in the same rotated order gives the same bits as the sweep."""
+    the step path in the same rotated order, with the sweep's workgroup shape
+    (256 query rows, one split), gives the same bits as the sweep."""
     x = workload_inputs("ring_anything")
     w = x["workload"]
     offs = ra.chunk_offsets(w.seq_len, w.n_chunks, True)
@@ -125,7 +126,7 @@ def test_sweep_rank_equals_its_shard(ra):
         for s in range(w.n_chunks):
             c = (r + s) % w.n_chunks
             ra.step(q_r, k[:, offs[c]:offs[c + 1]].contiguous(), v[:, offs[c]:offs[c + 1]].contiguous(), o_s, l_s,
-                    scale=x["scale"])
+                    scale=x["scale"], n_splits=1, block_m=256)
         torch.cuda.synchronize()
         assert torch.equal(o_s, out[:, lo:hi]) and torch.equal(l_s, lse[:, :, lo:hi]), f"rank {r}"
         d_out = (o_f - out[:, lo:hi]).abs().max().item()
