@@ -36,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "ringattn_acc_init_bf16",
     "ringattn_step_bf16",
     "ringattn_step_split",
+    "ringattn_forward_noalloc",
 )
 
 
@@ -120,6 +121,8 @@ _SIGNATURES = {
     "ringattn_acc_init_bf16": (ctypes.c_int, [_vp, _vp, _shape_p, _vp]),
     "ringattn_step_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _shape_p, _vp]),
     "ringattn_step_split": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _shape_p, _plan_p, _vp, _sz, _vp]),
+    "ringattn_forward_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _i64p, _i32, _i64, _vp, _vp, _f32, _shape_p, _plan_p,
+                                                _vp]),
 }
 
 

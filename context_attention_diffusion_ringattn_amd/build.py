@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libringattn.so")
 
-SOURCES = ["api.cpp", "attn_pp.hip", "attn_w3.hip", "merge.hip"]
+SOURCES = ["api.cpp", "attn_pp.hip", "attn_w3.hip", "merge.hip", "noalloc.hip"]
 
 # Packed fp32 VALU forms are disabled on purpose: the kernels are written with
 # plain fp32 arithmetic and must not be lowered to v_pk_{add,mul,fma}_f32.

@@ -333,11 +333,16 @@ int check_workspace(const Plan &p, void *workspace, size_t workspace_bytes) {
     return RINGATTN_OK;
 }
 
-// ringattn_forward with the plan restricted to workspaces of at most max_ws bytes.
-int forward_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
-                 int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
-                 const ringattn_shape *shape, const ringattn_plan *plan, void *workspace, size_t workspace_bytes,
-                 size_t max_ws, hipStream_t s) {
+}  // namespace
+
+namespace ringattn {
+
+// ringattn_forward's validation and launch plan, restricted to workspaces of
+// at most max_ws bytes; host code only (no HIP call).  *ws_needed: the
+// workspace bytes of the plan.
+int forward_check(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
+                  int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
+                  const ringattn_shape *shape, const ringattn_plan *plan, size_t max_ws, size_t *ws_needed) {
     int st;
     if ((st = check_shape(shape, true))) return st;
     if ((st = check_ptr(q, 16, "q"))) return st;
@@ -352,6 +357,24 @@ int forward_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const 
         if ((st = check_ptr(k, 16, "k"))) return st;
         if ((st = check_ptr(v, 16, "v"))) return st;
     }
+    *ws_needed = p.ws_bytes;
+    return RINGATTN_OK;
+}
+
+// ringattn_forward with the plan restricted to workspaces of at most max_ws bytes.
+int forward_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
+                 int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
+                 const ringattn_shape *shape, const ringattn_plan *plan, void *workspace, size_t workspace_bytes,
+                 size_t max_ws, hipStream_t s) {
+    int st;
+    size_t need = 0;
+    if ((st = forward_check(q, k, v, chunk_offsets, n_chunks, kv_chunk_stride, out, lse, scale, shape, plan, max_ws,
+                            &need)))
+        return st;
+    Layout L;
+    if ((st = build_layout(chunk_offsets, n_chunks, kv_chunk_stride, shape->kv_len, &L))) return st;
+    Plan p;
+    if ((st = make_plan(shape, L, plan ? plan->n_splits : 0, plan ? plan->block_m : 0, &p, max_ws))) return st;
     if ((st = check_workspace(p, workspace, workspace_bytes))) return st;
     if (L.ct.n_tiles == 0) {  // no keys at all: the empty result
         const int64_t n_out = (int64_t)shape->batch * shape->q_len * shape->heads * shape->head_dim;
@@ -361,7 +384,9 @@ int forward_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const 
     return run_planned(q, k, v, out, lse, scale, shape, L, p, workspace, false, s);
 }
 
-}  // namespace
+int report_error(int status, const char *message) { return fail(status, "%s", message); }
+
+}  // namespace ringattn
 
 extern "C" {
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ringattn.h"
+
 namespace ringattn {
 
 constexpr int kMaxChunks = 128;   // == RINGATTN_MAX_CHUNKS
@@ -85,5 +87,19 @@ hipError_t launch_merge2(float *out_acc, float *lse_acc, const float *out_part, 
                          int64_t q_len, int32_t batch, int32_t heads, int32_t head_dim, hipStream_t stream);
 hipError_t launch_acc_init(float *out, float *lse, int64_t n_out, int64_t n_lse, hipStream_t stream);
 hipError_t launch_acc_init_bf16(uint16_t *out, uint16_t *lse, int64_t n_out, int64_t n_lse, hipStream_t stream);
+
+// Host side of the C ABI (api.cpp), for entry points defined elsewhere.
+// forward_check: ringattn_forward's validation and plan with the workspace
+// limited to max_ws bytes (no HIP call); forward_impl: the same call, run
+// with `workspace`; report_error: set the message of ringattn_last_error().
+int forward_check(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
+                  int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
+                  const ::ringattn_shape *shape, const ::ringattn_plan *plan, size_t max_ws,
+                  size_t *ws_needed);
+int forward_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *chunk_offsets,
+                 int32_t n_chunks, int64_t kv_chunk_stride, float *out, float *lse, float scale,
+                 const ::ringattn_shape *shape, const ::ringattn_plan *plan, void *workspace,
+                 size_t workspace_bytes, size_t max_ws, hipStream_t s);
+int report_error(int status, const char *message);
 
 }  // namespace ringattn

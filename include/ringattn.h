@@ -209,6 +209,26 @@ int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      const ringattn_plan *plan, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ringattn_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid allocation):
+ * the same arguments without the workspace, the same result.  The split
+ * workspace of its launch plan is a fixed device array of
+ * RINGATTN_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
+ * until the process ends.  With plan NULL (or n_splits 0) the library
+ * chooses among the plans whose workspace fits that array; a requested plan
+ * whose workspace does not fit is rejected with RINGATTN_EWORKSPACE before
+ * anything is launched.  The call itself allocates nothing.  Calls on one GPU
+ * share its array and need none of its contents from an earlier call:
+ * calls that overlap in time on one GPU (different streams, not ordered)
+ * race on it and must be avoided by the caller.
+ */
+#define RINGATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ringattn_forward_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const int64_t *chunk_offsets, int32_t n_chunks, int64_t kv_chunk_stride,
+                             float *out, float *lse, float scale, const ringattn_shape *shape,
+                             const ringattn_plan *plan, void *stream);
+
+/*
  * The whole ring on one GPU: all n_chunks ranks of a ring over a sequence of
  * S = shape->q_len = shape->kv_len tokens.  Rank r holds query rows
  * [offsets[r], offsets[r+1]) and K/V chunk r (chunk_offsets as in

@@ -324,3 +324,25 @@ def test_workspace_layout(L):
         assert st == 0 and plan.n_splits == splits
         lse_off = a16(splits * B * Sq * H * D * 4)
         assert plan.workspace_bytes == a16(lse_off + splits * B * H * Sq * 4)
+
+
+def _noalloc(L, offs, s, splits=0, block_m=0, q=P, k=P, v=P, out=P, lse=P, scale=0.125, stride=0):
+    arr = _lib.offsets_array(offs)
+    plan = _lib.Plan(n_splits=splits, block_m=block_m, workspace_bytes=0)
+    return L.ringattn_forward_noalloc(q, k, v, arr, len(offs) - 1, stride, out, lse, ctypes.c_float(scale),
+                                      ctypes.byref(s), ctypes.byref(plan), None)
+
+
+def test_forward_noalloc_validation(L):
+    """The no-allocation forward validates like ringattn_forward before any
+    HIP call, and rejects a requested plan whose workspace exceeds its fixed
+    64 MiB scratch array with RINGATTN_EWORKSPACE and a message saying so."""
+    s = shape(B=1, H=24, D=128, Sq=16384, Skv=16384)
+    st, plan = _plan(L, s, [0, 16384], splits=4, block_m=256)
+    assert st == 0 and plan.workspace_bytes > (64 << 20)
+    assert _noalloc(L, [0, 16384], s, splits=4, block_m=256) == _lib.RINGATTN_EWORKSPACE
+    assert "workspace" in _lib.last_error()
+    assert _noalloc(L, [0, 16384], s, q=None) == _lib.RINGATTN_EINVAL
+    assert _noalloc(L, [0, 16384], s, scale=-1.0) == _lib.RINGATTN_EINVAL
+    assert _noalloc(L, [0, 100], s) == _lib.RINGATTN_EINVAL
+    assert _noalloc(L, [0, 16384], shape(D=32, Sq=16384, Skv=16384)) == _lib.RINGATTN_EUNSUPPORTED
