@@ -11,7 +11,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
+# RINGATTN_LIB selects another build of the same library (the sanitizer
+# build of build.py); by default the in-tree libringattn.so.
+LIB_PATH = os.environ.get("RINGATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libringattn.so")
 
 RINGATTN_OK = 0
 RINGATTN_EINVAL = -1
