@@ -2,14 +2,20 @@
 accumulators (ringattn_step_bf16) against the oracle's bf16-state ring, and
 the error of both merge precisions against exact one-shot attention.
 
-Tolerance, from the arithmetic: both sides store bf16(value) after every
-step; they may differ by one bf16 ulp where a value lies near a rounding
-boundary, and the GPU's float32 partial differs from the fp64 one by
-<= ~3e-3 (bf16 probabilities in PV).  With N steps and merge weights <= 1:
-|d lse| <= 1 ulp(lse); |d out| <= 2 N ulp(|out|) + 1e-2 -- required for
-99.9 % of the elements; a one-ulp LSE flip in an intermediate step moves
-the merge weights by up to ulp(lse) (~0.03-0.06), so every element must be
-within 0.1 max|out| + 2 N ulp.
+Tolerance, from the arithmetic, for every element.  Both sides store
+bf16(value) after every step; they may differ by one bf16 ulp where a value
+lies near a rounding boundary, and the GPU's float32 partial differs from the
+fp64 one by <= ~3e-3 (bf16 probabilities in PV).  A step merges the stored
+state (a = its LSE, acc) with the chunk partial (b, part):
+out' = w_a acc + w_b part with w_a = exp(a - lse'), w_b = exp(b - lse'),
+and d out' / d a = -d out' / d b = w_a w_b (acc - part).  So a one-ulp
+difference in the stored or the partial LSE moves that step's output by at
+most (ulp(a) + ulp(b)) w_a w_b |acc - part|, and later merges scale it by
+weights <= 1.  Per element:
+  |d lse| <= 1 ulp(lse);
+  |d out| <= sum over steps of (ulp(a) + ulp(b)) w_a w_b |acc - part|
+             + 2 N ulp(out) + 1e-2,
+with the steps' a, b, acc and part taken from the oracle twin's states.
 """
 
 import numpy as np
@@ -34,6 +40,35 @@ def ra():
 def ulp_bf16(x):
     a = np.maximum(np.abs(x), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def round_bf16(x):
+    """Round to the nearest bf16 (ties to even) and back to float64."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def lse_flip_bound(q64, k64, v64, offs, scale):
+    """Per-element sum over the ring's steps of (ulp(a) + ulp(b)) w_a w_b
+    |acc - part|, from the oracle's bf16-state ring (its partials and stored
+    states, rounded to bf16 as the twin rounds them)."""
+    B, Sq, H, D = q64.shape
+    acc = np.zeros((B, Sq, H, D))
+    a = np.full((B, H, Sq), -np.inf)
+    bound = np.zeros((B, Sq, H, D))
+    for c in range(len(offs) - 1):
+        part, b = oracle.chunk_partial_fp64(q64, k64[:, offs[c]:offs[c + 1]], v64[:, offs[c]:offs[c + 1]], scale)
+        part, b = round_bf16(part), round_bf16(b)
+        both = np.isfinite(a) & np.isfinite(b)
+        m = np.where(both, np.maximum(a, b), 0.0)
+        lse_new = np.where(both, m + np.log(np.exp(np.where(both, a, 0) - m) + np.exp(np.where(both, b, 0) - m)),
+                           0.0)
+        wab = np.where(both, np.exp(np.where(both, a, 0) - lse_new) * np.exp(np.where(both, b, 0) - lse_new), 0.0)
+        du = np.where(both, ulp_bf16(np.where(both, a, 1.0)) + ulp_bf16(np.where(both, b, 1.0)), 0.0)
+        step = (du * wab).transpose(0, 2, 1)[..., None]  # [B, Sq, H, 1]
+        bound += step * np.abs(acc - part)
+        acc, a = oracle.lse_merge_fp64(acc, a, part, b)
+        acc, a = round_bf16(acc), round_bf16(a)
+    return bound
 
 
 def run_ring(ra, q, k, v, offs, scale, bf16):
@@ -67,13 +102,13 @@ def test_bf16_state_ring(ra, name):
     fo, fl = run_ring(ra, q, k, v, offs, x["scale"], bf16=False)
     go, gl, fo, fl = go[:, rows], gl[:, :, rows], fo[:, rows], fl[:, :, rows]
     n = len(offs) - 1
-    # parity of the bf16-state path with its oracle
+    # parity of the bf16-state path with its oracle, element by element
     assert np.all(np.abs(gl - ref_l) <= ulp_bf16(ref_l) * 1.0001), "lse beyond one bf16 ulp"
-    tol = 2 * n * ulp_bf16(ref_o) + 1e-2
-    frac = float(np.mean(np.abs(go - ref_o) <= tol))
-    worst = float(np.max(np.abs(go - ref_o) - 2 * n * ulp_bf16(ref_o)))
-    assert frac >= 0.999, f"only {frac:.5f} of the elements within tolerance"
-    assert worst <= 0.1 * float(np.max(np.abs(ref_o))), worst
+    flip = lse_flip_bound(q64[:, rows], k64, v64, offs, x["scale"])
+    tol = flip + 2 * n * ulp_bf16(ref_o) + 1e-2
+    err = np.abs(go - ref_o)
+    frac = float(np.mean(err <= 2 * n * ulp_bf16(ref_o) + 1e-2))  # share inside the bound without the flip term
+    assert np.all(err <= tol), f"{int(np.sum(err > tol))} elements beyond the bound, worst {float(np.max(err - tol)):.3e}"
     # the study: both merge precisions against exact attention
     e32o, e32l = float(np.max(np.abs(fo - ex_o))), float(np.max(np.abs(fl - ex_l)))
     e16o, e16l = float(np.max(np.abs(go - ex_o))), float(np.max(np.abs(gl - ex_l)))
