@@ -37,8 +37,9 @@ PEAK_HBM_GBS = 8000.0
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200,
+                    help="timed steps (default 200: about 1.1 s of kernels on the video shard)")
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="video",
                     help="tiny | flux | ring_anything | ring_even | ulysses | ulysses_anything | ulysses_even | usp | video (default: video)")
     ap.add_argument("--splits", type=int, default=0, help="force the K/V split count (0 = library plan)")

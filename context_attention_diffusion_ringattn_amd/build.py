@@ -61,12 +61,35 @@ def _compile(hipcc: str, src: str, verbose: bool) -> str:
     return obj
 
 
+PROBE_DIR = os.path.join(PKG_DIR, "probes")
+PROBE_BIN = os.path.join(BUILD_DIR, "probes")
+PROBES = ["issue_probe.hip", "lds_probe.hip"]
+
+
+def _compile_probe(hipcc: str, src: str, verbose: bool) -> str:
+    """A hardware probe (a stand-alone program, not part of the library)."""
+    exe = os.path.join(PROBE_BIN, os.path.splitext(src)[0])
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", os.path.join(PROBE_DIR, src), "-o", exe]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling probe {src} failed:\n{res.stdout}{res.stderr}")
+    return exe
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libringattn.so`` next to this file."""
+    """Compile every source and link ``libringattn.so`` next to this file; also
+    build the hardware probes under ``_build/probes``."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    os.makedirs(PROBE_BIN, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBES)) as ex:
+        probes = [ex.submit(_compile_probe, hipcc, p, verbose) for p in PROBES]
         objs = list(ex.map(lambda s: _compile(hipcc, s, verbose), SOURCES))
+        for p in probes:
+            p.result()
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
