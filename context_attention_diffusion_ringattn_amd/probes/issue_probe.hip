@@ -142,10 +142,20 @@ int main(int argc, char **argv) {
     run<2, 1, 0, 0>(256, iters);
     run<3, 1, 0, 0>(256, iters);
     run<4, 1, 0, 0>(256, iters);
+    run<6, 1, 0, 0>(256, iters);
+    run<0, 2, 0, 0>(256, iters);
+    run<2, 2, 0, 0>(256, iters);
+    run<4, 2, 0, 0>(256, iters);
+    run<0, 3, 0, 0>(256, iters);
+    run<0, 4, 0, 0>(256, iters);
     run<0, 0, 1, 0>(256, iters);
     run<0, 0, 2, 0>(256, iters);
     run<3, 1, 2, 0>(256, iters);
     run<3, 1, 1, 0>(256, iters);
+    run<4, 1, 0, 0>(512, iters / 2);
+    run<3, 1, 2, 0>(512, iters / 2);
+    run<3, 1, 1, 0>(512, iters / 2);
+    run<4, 2, 1, 0>(512, iters / 2);
     run<4, 1, 0, 1>(512, iters);
     run<4, 2, 0, 1>(512, iters);
     const hipError_t e = hipDeviceSynchronize();
