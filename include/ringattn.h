@@ -90,6 +90,10 @@ int32_t ringattn_abi_version(void);
  *     chunks hold one extra token, so every chunk fits the padded length
  *     ceil(seq_len / n_chunks) that Ring Anything pads to.
  * n_chunks must be in [1, RINGATTN_MAX_CHUNKS].  Pure host code.
+ * Source: context parallelism guide, variant table (plain ring needs an
+ * evenly divisible sequence) and section "Ring Anything Attention" (uneven
+ * chunks padded to the longest); Parallelism API page,
+ * ContextParallelConfig.ring_degree and ring_anything.
  */
 int ringattn_chunk_offsets(int64_t seq_len, int32_t n_chunks, int32_t ring_anything,
                            int64_t *offsets_out);
@@ -98,6 +102,9 @@ int ringattn_chunk_offsets(int64_t seq_len, int32_t n_chunks, int32_t ring_anyth
  * Set a float32 accumulator to the empty merge state: out_acc = 0 and
  * lse_acc = -inf (the identity of the LSE merge).  out_acc is
  * [B, q_len, H, D], lse_acc is [B, H, q_len].  shape->kv_len is ignored.
+ * Source: the float32 merge state of Parallelism API page,
+ * ContextParallelConfig.convert_to_fp32, before the ring's first iteration
+ * (context parallelism guide, section "Ring Attention").
  */
 int ringattn_acc_init(float *out_acc, float *lse_acc, const ringattn_shape *shape, void *stream);
 
@@ -115,6 +122,10 @@ int ringattn_acc_init(float *out_acc, float *lse_acc, const ringattn_shape *shap
  * shard's attention output and LSE.  scale must be finite and > 0.  One
  * workgroup sweeps each query tile over the whole chunk (no workspace);
  * ringattn_step_split below can spread the chunk's keys over several.
+ * Source: context parallelism guide, section "Ring Attention" (one attention
+ * pass per iteration on the K/V chunk the GPU holds, N iterations for a ring
+ * of degree N); Parallelism API page, ContextParallelConfig.convert_to_fp32
+ * (output and LSE in float32 for the merge).
  */
 int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_chunk,
                   float *out_acc, float *lse_acc, float scale,
@@ -125,6 +136,9 @@ int ringattn_step(const uint16_t *q, const uint16_t *k_chunk, const uint16_t *v_
  * into the accumulators in place, with the same formula as ringattn_step.
  * A partial with lse = -inf is the identity; if both are -inf the result is
  * out = 0, lse = -inf.  shape->kv_len is ignored.
+ * Source: the float32 merge of chunk partials by their LSE (Parallelism API
+ * page, ContextParallelConfig.convert_to_fp32; context parallelism guide,
+ * section "Ring Attention").
  */
 int ringattn_merge(float *out_acc, float *lse_acc, const float *out_part, const float *lse_part,
                    const ringattn_shape *shape, void *stream);
@@ -175,6 +189,7 @@ int ringattn_step_split(const uint16_t *q, const uint16_t *k_chunk, const uint16
  * Fill *plan (see ringattn_plan) for a ringattn_forward call with these
  * arguments.  Pure host code: validates like ringattn_forward and launches
  * nothing.  Plans are deterministic for a given shape, layout and device.
+ * (A launch choice of this library; the pages define no plan.)
  */
 int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offsets, int32_t n_chunks,
                           int64_t kv_chunk_stride, ringattn_plan *plan);
@@ -202,6 +217,12 @@ int ringattn_forward_plan(const ringattn_shape *shape, const int64_t *chunk_offs
  * (RINGATTN_EWORKSPACE otherwise); workspace may be NULL with
  * workspace_bytes = 0 only when the plan needs none.  With kv_len = 0 the
  * result is out = 0, lse = -inf.
+ * Source: context parallelism guide, section "Ring Attention" (after one
+ * full turn every GPU has attended to the K/V of all tokens; with
+ * rotate_method "allgather" every chunk is resident at once), section "Ring
+ * Anything Attention" (the padded buffer) and section "Perhatian Ulysses"
+ * (the Ulysses share is this call with one chunk); Parallelism API page,
+ * ContextParallelConfig.
  */
 int ringattn_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      const int64_t *chunk_offsets, int32_t n_chunks, int64_t kv_chunk_stride,
