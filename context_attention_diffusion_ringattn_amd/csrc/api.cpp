@@ -262,7 +262,11 @@ hipError_t launch_plan(AttnArgs a, const Plan &p, const Layout &L, int head_dim,
         return launch_attn_pp(a, head_dim, mode, L.chunked, s);
     }
     a.ct = L.ct32;
-    return launch_attn_w3(a, head_dim, mode, L.chunked, s);
+    // a launch that leaves each CU at most one workgroup runs it as two key
+    // groups (8 waves) instead of one 4-wave workgroup
+    const int64_t grid = (int64_t)p.n_qtiles * a.heads * a.batch * p.n_splits;
+    const int key_groups = grid <= cu_count_for_current_device() ? 2 : 1;
+    return launch_attn_w3(a, head_dim, key_groups, mode, L.chunked, s);
 }
 
 void fill_common(AttnArgs *a, const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,

@@ -1,5 +1,6 @@
-// attn_w3.hip -- ring-shard attention kernel for gfx950 with three
-// workgroups per compute unit.
+// attn_w3.hip -- ring-shard attention kernel for gfx950 with 128 query rows
+// per workgroup: three workgroups per compute unit, or (for launches of at
+// most one workgroup per compute unit) one workgroup of two key groups.
 //
 // Same computation as attn_pp.hip (one non-causal softmax-attention sweep of
 // a query block over K/V tiles; the running float32 (max, sum, output) state
@@ -21,6 +22,13 @@
 //    float32 row sums), O^T += V^T P^T as 8 MFMAs with V^T from transposing
 //    LDS reads.
 //  * At most 168 VGPRs per wave, so that three waves fit a SIMD.
+//  * Key groups (KG = 2): when a launch has no more workgroups than compute
+//    units, a CU would hold one 4-wave workgroup, one wave per SIMD.  Then
+//    the workgroup runs 8 waves in two key groups over the same 128 rows:
+//    group g sweeps tiles t_lo + g, t_lo + g + 2, ... with its own three
+//    stages, and at the end the second group hands its partial state to the
+//    first through LDS, which merges the two by their row maxima (the LSE
+//    merge of two partials of the same rows) before the epilogue.
 #include "attn_tiles.h"
 
 #include <math.h>
@@ -31,13 +39,25 @@ namespace ringattn {
 namespace {
 
 constexpr int kW3Waves = 4;
-constexpr int kW3Threads = 64 * kW3Waves;
 constexpr int kW3BlockM = 32 * kW3Waves;  // 128 query rows per workgroup
 constexpr int kW3BlockN = 32;             // keys per tile
 constexpr int kW3Stages = 3;
 
-template <int D>
+typedef __attribute__((address_space(3))) float lds_float;
+
+template <int D, int KG>
 struct W3Geo {
+    static constexpr int WAVES = kW3Waves * KG;           // KG key groups of 4 row waves
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int GROUP_LDS = 2 * kW3Stages * kW3BlockN * D * 2;  // one key group's stages
+    // with two key groups, the second hands its state to the first past the
+    // first group's staging slices: D/2 + 2 words per lane of 4 waves
+    static constexpr int XBASE = kW3Waves * kStageBytes;
+    static constexpr int XWORDS = D / 32 * 16 + 2;
+    static constexpr int LDS_BYTES = KG == 1 ? GROUP_LDS
+                                     : (KG * GROUP_LDS > XBASE + XWORDS * 4 * 64 * kW3Waves
+                                            ? KG * GROUP_LDS
+                                            : XBASE + XWORDS * 4 * 64 * kW3Waves);
     static constexpr int ROW = D * 2;                     // bytes per K/V row
     static constexpr int KCH = D / 8;                     // 16-byte pieces per row
     static constexpr int TILE = kW3BlockN * ROW;          // bytes of one K (or V) tile
@@ -47,18 +67,21 @@ struct W3Geo {
     static_assert(LPW >= 1 && LPW * kW3Waves * 1024 == TILE, "tile split over waves");
 };
 
-template <int D, int MODE, bool CHUNKED>
-__global__ __launch_bounds__(kW3Threads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+template <int D, int MODE, bool CHUNKED, int KG>
+__global__ __launch_bounds__((W3Geo<D, KG>::THREADS)) __attribute__((amdgpu_waves_per_eu(KG == 1 ? 3 : 2, KG == 1 ? 3 : 2)))
 void attn_w3_kernel(const AttnArgs a) {
-    using G = W3Geo<D>;
-    // Three stages: V tiles in [0, 3*TILE), K tiles in [3*TILE, 6*TILE).
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kW3Stages * G::TILE];
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_byte *)smem;
-    constexpr uint32_t kKRegion = kW3Stages * G::TILE;
-
+    using G = W3Geo<D, KG>;
+    // Per key group, three stages: V tiles in [0, 3*TILE), K tiles in
+    // [3*TILE, 6*TILE) of the group's region.
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave_id / kW3Waves;   // key group: tiles t_lo + kg, t_lo + kg + KG, ...
+    const int wave = wave_id % kW3Waves; // row wave: query rows 32 wave .. 32 wave + 31
+    const uint32_t lds_all = (uint32_t)(uintptr_t)(lds_byte *)smem;
+    const uint32_t lds0 = lds_all + (uint32_t)kg * G::GROUP_LDS;
+    constexpr uint32_t kKRegion = kW3Stages * G::TILE;
     const int col = lane & 31;   // query row within the wave's 32 rows
     const int half = lane >> 5;  // which 32-lane half
 
@@ -236,25 +259,30 @@ void attn_w3_kernel(const AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 2, 1);
     };
 
-    // ---- sweep: tile t in stage t % 3, loads issued two tiles ahead ----------
-    // Tile t's loads are issued at the start of tile t-2 (into the stage that
-    // tile t-3 used, released by the barrier at the end of tile t-3) and
-    // waited for before the barrier at the end of tile t-1, which publishes
-    // them to the whole workgroup.
+    // ---- sweep: step j is tile t_lo + KG j + kg of each key group, in stage
+    // j % 3; loads issued two steps ahead ------------------------------------
+    // A group's step-j tile's loads are issued at the start of step j-2 (into
+    // the stage that its step j-3 used, released by the barrier at the end of
+    // step j-3) and waited for before the barrier at the end of step j-1,
+    // which publishes them to the whole workgroup.  The groups step together;
+    // a group past its last tile only takes part in the barriers.
+    const int Tg = (T - kg + KG - 1) / KG;   // this group's tiles
+    const int Ts = (T + KG - 1) / KG;        // steps (the first group's tiles)
+    auto tile_of = [&](int j) __attribute__((always_inline)) { return t_lo + KG * j + kg; };
     constexpr std::integral_constant<int, 0> I0{};
     constexpr std::integral_constant<int, 1> I1{};
     constexpr std::integral_constant<int, 2> I2{};
-    if (T > 0) issue_loads(I0, t_lo);
-    if (T > 1) issue_loads(I1, t_lo + 1);
+    if (Tg > 0) issue_loads(I0, tile_of(0));
+    if (Tg > 1) issue_loads(I1, tile_of(1));
     wait_vmcnt<0>();
     wg_barrier();
     auto step = [&](auto sc, auto sl, int j) __attribute__((always_inline)) -> bool {
-        if (j >= T) return false;
-        if (j + 2 < T) issue_loads(sl, t_lo + j + 2);
+        if (j >= Ts) return false;
+        if (j + 2 < Tg) issue_loads(sl, tile_of(j + 2));
         __builtin_amdgcn_sched_barrier(0);
-        compute(sc, t_lo + j);
+        if (j < Tg) compute(sc, tile_of(j));
         __builtin_amdgcn_sched_barrier(0);
-        if (j + 2 < T) wait_vmcnt<G::VM_PER_TILE>();
+        if (j + 2 < Tg) wait_vmcnt<G::VM_PER_TILE>();
         else wait_vmcnt<0>();
         wg_barrier();
         return true;
@@ -265,12 +293,46 @@ void attn_w3_kernel(const AttnArgs a) {
         if (!step(I2, I1, j + 2)) break;
     }
 
+    float l_lane = l0 + l1;
+    if constexpr (KG == 2) {
+        // The second key group hands its partial state (O, the row max, this
+        // lane's share of the row sum) through LDS, past the staging slices
+        // of the first group's epilogue; the first group merges it with its
+        // own by their maxima (the LSE merge of two partials of the same rows).
+        constexpr int kWords = G::XWORDS;
+        constexpr uint32_t kXBase = G::XBASE;
+        const uint32_t xa = lds_all + kXBase + (uint32_t)(wave * 64 + lane) * 4;
+        auto xat = [&](int k) __attribute__((always_inline)) { return (lds_float *)(uintptr_t)(xa + (uint32_t)k * 64 * kW3Waves * 4); };
+        if (kg == 1) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) *xat(db * 16 + v) = o[db][v];
+            *xat(kWords - 2) = m_run;
+            *xat(kWords - 1) = l_lane;
+        }
+        wg_barrier();
+        if (kg == 1) return;
+        const float m1 = *xat(kWords - 2);
+        const float l1s = *xat(kWords - 1);
+        const float m = fmaxf(m_run, m1);
+        // a side still at -inf (no keys) has nothing to add: its factor is
+        // never formed from -inf - -inf
+        const float a0 = m_run == m ? 1.f : fast_exp2((m_run - m) * sl2);
+        const float a1 = m1 == m ? 1.f : fast_exp2((m1 - m) * sl2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[db][v] = o[db][v] * a0 + *xat(db * 16 + v) * a1;
+        l_lane = l_lane * a0 + l1s * a1;
+        m_run = m;
+    }
+
     // ---- epilogue -------------------------------------------------------------
-    const float l_lane = l0 + l1;
     const float l_tot = l_lane + other_half(l_lane, half != 0);
     if constexpr (MODE == kModeFinal || MODE == kModePartial) {
         // every wave passed the barrier after the last tile: the stages are free
-        static_assert(kW3Waves * kStageBytes <= sizeof(smem), "staging fits the stages");
+        static_assert(kW3Waves * kStageBytes <= G::GROUP_LDS, "staging fits the stages");
         write_rows_staged<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow - col, a.q_len, split, lane,
                                    lds0 + (uint32_t)wave * kStageBytes);
     } else {
@@ -278,35 +340,44 @@ void attn_w3_kernel(const AttnArgs a) {
     }
 }
 
-template <int D, bool CHUNKED>
+template <int D, bool CHUNKED, int KG>
 hipError_t launch_w3_dc(const AttnArgs &a, EpilogueMode mode, hipStream_t stream) {
     const int64_t grid = (int64_t)a.n_qtiles * a.heads * a.batch * a.n_splits;
+    constexpr int kW3Threads = W3Geo<D, KG>::THREADS;
     switch (mode) {
         case kModeFinal:
-            hipLaunchKernelGGL((attn_w3_kernel<D, kModeFinal, CHUNKED>), dim3((unsigned)grid), dim3(kW3Threads), 0,
+            hipLaunchKernelGGL((attn_w3_kernel<D, kModeFinal, CHUNKED, KG>), dim3((unsigned)grid), dim3(kW3Threads), 0,
                                stream, a);
             break;
         case kModePartial:
-            hipLaunchKernelGGL((attn_w3_kernel<D, kModePartial, CHUNKED>), dim3((unsigned)grid), dim3(kW3Threads),
+            hipLaunchKernelGGL((attn_w3_kernel<D, kModePartial, CHUNKED, KG>), dim3((unsigned)grid), dim3(kW3Threads),
                                0, stream, a);
             break;
         case kModeAccum:
-            hipLaunchKernelGGL((attn_w3_kernel<D, kModeAccum, CHUNKED>), dim3((unsigned)grid), dim3(kW3Threads), 0,
+            hipLaunchKernelGGL((attn_w3_kernel<D, kModeAccum, CHUNKED, KG>), dim3((unsigned)grid), dim3(kW3Threads), 0,
                                stream, a);
             break;
         case kModeAccumBf16:
-            hipLaunchKernelGGL((attn_w3_kernel<D, kModeAccumBf16, CHUNKED>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((attn_w3_kernel<D, kModeAccumBf16, CHUNKED, KG>), dim3((unsigned)grid),
                                dim3(kW3Threads), 0, stream, a);
             break;
     }
     return hipGetLastError();
 }
 
+template <int KG>
+hipError_t launch_w3_kg(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream) {
+    if (head_dim == 128)
+        return chunked ? launch_w3_dc<128, true, KG>(a, mode, stream) : launch_w3_dc<128, false, KG>(a, mode, stream);
+    return chunked ? launch_w3_dc<64, true, KG>(a, mode, stream) : launch_w3_dc<64, false, KG>(a, mode, stream);
+}
+
 }  // namespace
 
-hipError_t launch_attn_w3(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream) {
-    if (head_dim == 128) return chunked ? launch_w3_dc<128, true>(a, mode, stream) : launch_w3_dc<128, false>(a, mode, stream);
-    return chunked ? launch_w3_dc<64, true>(a, mode, stream) : launch_w3_dc<64, false>(a, mode, stream);
+hipError_t launch_attn_w3(const AttnArgs &a, int head_dim, int key_groups, EpilogueMode mode, bool chunked,
+                          hipStream_t stream) {
+    return key_groups == 2 ? launch_w3_kg<2>(a, head_dim, mode, chunked, stream)
+                           : launch_w3_kg<1>(a, head_dim, mode, chunked, stream);
 }
 
 }  // namespace ringattn

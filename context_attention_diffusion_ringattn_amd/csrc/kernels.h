@@ -77,7 +77,10 @@ struct MergeSplitsArgs {
 
 // 4-wave, 128-row variant (three workgroups per CU, 32-key tiles; the chunk
 // table counts 32-key tiles).
-hipError_t launch_attn_w3(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream);
+// key_groups: 1 (three 4-wave workgroups per CU) or 2 (one 8-wave workgroup
+// of two key groups per CU, for launches of at most one workgroup per CU)
+hipError_t launch_attn_w3(const AttnArgs &a, int head_dim, int key_groups, EpilogueMode mode, bool chunked,
+                          hipStream_t stream);
 // 8-wave, 256-row variant; `chunked` = walk the chunk table (padded layout).
 hipError_t launch_attn_pp(const AttnArgs &a, int head_dim, EpilogueMode mode, bool chunked, hipStream_t stream);
 // One ring step of several ranks in one launch (8-wave kernel, in-place float32 merge).
