@@ -9,7 +9,8 @@
 // operand.  Measured per wave with s_memtime: cycles per MFMA slot; from the
 // wall clock: the engine clock and the matrix rate.  A second mode runs two
 // waves per SIMD with one doing only the MFMAs and the other only the vector
-// ops, the arrangement of a ping-pong schedule.
+// ops, the arrangement of a ping-pong schedule (the role is chosen outside
+// the loops: neither stream carries a per-slot branch).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -48,25 +49,40 @@ __global__ __launch_bounds__(512) void issue_kernel(float *sink, int iters, long
     const float c1 = sink[0] + 0.999f, c2 = sink[1] + 1e-4f;
     const unsigned lbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)dyn + lane * 16 + wave * 1024;
     const long long t0 = __builtin_readcyclecounter();
-    for (int it = 0; it < iters; ++it) {
+    // One slot: an MFMA and/or the vector work.  The role test sits outside
+    // the loops, so that neither stream carries a branch per slot.
+    auto slot = [&](int it, int m, bool mf, bool va) __attribute__((always_inline)) {
+        if (mf) {
+            acc[m & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(LDSPER ? aop[m & 3] : a, b, acc[m & 7], 0, 0, 0);
+            if (LDSPER && (m % LDSPER) == 0)
+                aop[m & 3] = *(lds_bf16x8 *)(uintptr_t)(lbase + ((unsigned)(m * 4096 + it * 64) & 32767u));
+        }
+        if (va) {
 #pragma unroll
-        for (int m = 0; m < 64; ++m) {
-            if (do_mfma) {
-                acc[m & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(LDSPER ? aop[m & 3] : a, b, acc[m & 7], 0, 0, 0);
-                if (LDSPER && (m % LDSPER) == 0)
-                    aop[m & 3] = *(lds_bf16x8 *)(uintptr_t)(lbase + ((unsigned)(m * 4096 + it * 64) & 32767u));
-            }
-            if (do_valu) {
+            for (int v = 0; v < NV; ++v) x[(m * NV + v) & 15] = fmaf(x[(m * NV + v) & 15], c1, c2);
 #pragma unroll
-                for (int v = 0; v < NV; ++v) x[(m * NV + v) & 15] = fmaf(x[(m * NV + v) & 15], c1, c2);
+            for (int e = 0; e < NE; ++e) z[(m * NE + e) & 7] += __builtin_amdgcn_exp2f(y[(m * NE + e) & 7]);
+        }
+        if (mf && va) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (NV + 2 * NE) __builtin_amdgcn_sched_group_barrier(0x002, NV + 2 * NE, 0);
+            if (LDSPER && (m % LDSPER) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+    if (ROLE == 0) {
+        for (int it = 0; it < iters; ++it) {
 #pragma unroll
-                for (int e = 0; e < NE; ++e) z[(m * NE + e) & 7] += __builtin_amdgcn_exp2f(y[(m * NE + e) & 7]);
-            }
-            if (ROLE == 0) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (NV + 2 * NE) __builtin_amdgcn_sched_group_barrier(0x002, NV + 2 * NE, 0);
-                if (LDSPER && (m % LDSPER) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
+            for (int m = 0; m < 64; ++m) slot(it, m, true, true);
+        }
+    } else if (do_mfma) {
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int m = 0; m < 64; ++m) slot(it, m, true, false);
+        }
+    } else if (do_valu) {
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int m = 0; m < 64; ++m) slot(it, m, false, true);
         }
     }
     const long long t1 = __builtin_readcyclecounter();
