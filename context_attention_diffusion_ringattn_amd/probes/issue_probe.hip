@@ -2,11 +2,12 @@
 // v_mfma_f32_32x32x16_bf16 and the softmax's vector work.
 //
 // One workgroup per compute unit (96 KB of LDS each forces that); every wave
-// runs ITERS x 64 MFMAs on register operands (8 independent accumulators)
-// and, between consecutive MFMAs, NV fma-class VALU ops, NE exp2 (each on an
-// independent register, followed by an add), and one 16-byte LDS read every
-// LDSPER MFMAs (LDSPER = 0: none) whose result feeds a later MFMA as its A
-// operand.  Measured per wave with s_memtime: cycles per MFMA slot; from the
+// runs ITERS x 64 MFMAs on register operands (NCH independent accumulator
+// chains, 8 unless stated) and, between consecutive MFMAs, NV fma-class VALU
+// ops, NE exp2 (each on an independent register, followed by an add), and one
+// 16-byte LDS read every LDSPER MFMAs (LDSPER = 0: none) whose result feeds a
+// later MFMA as its A operand.  About half a second of MFMA work runs first,
+// so that every row is timed at the loaded engine clock.  Measured per wave with s_memtime: cycles per MFMA slot; from the
 // wall clock: the engine clock and the matrix rate.  A second mode runs two
 // waves per SIMD with one doing only the MFMAs and the other only the vector
 // ops, the arrangement of a ping-pong schedule (the role is chosen outside
@@ -24,7 +25,7 @@ constexpr size_t kLds = 96 * 1024;
 
 // ROLE 0: every wave runs the mixed stream.  ROLE 1: waves 0-3 run only the
 // MFMAs, waves 4-7 (same SIMDs) only the vector ops.
-template <int NV, int NE, int LDSPER, int ROLE>
+template <int NV, int NE, int LDSPER, int ROLE, int NCH>
 __global__ __launch_bounds__(512) void issue_kernel(float *sink, int iters, long long *cycles) {
     extern __shared__ char dyn[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(512) void issue_kernel(float *sink, int iters, long
     // the loops, so that neither stream carries a branch per slot.
     auto slot = [&](int it, int m, bool mf, bool va) __attribute__((always_inline)) {
         if (mf) {
-            acc[m & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(LDSPER ? aop[m & 3] : a, b, acc[m & 7], 0, 0, 0);
+            acc[m % NCH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(LDSPER ? aop[m & 3] : a, b, acc[m % NCH], 0, 0, 0);
             if (LDSPER && (m % LDSPER) == 0)
                 aop[m & 3] = *(lds_bf16x8 *)(uintptr_t)(lbase + ((unsigned)(m * 4096 + it * 64) & 32767u));
         }
@@ -99,9 +100,9 @@ static int g_cus = 256;
 static float *g_sink;
 static long long *g_cyc;
 
-template <int NV, int NE, int LDSPER, int ROLE>
+template <int NV, int NE, int LDSPER, int ROLE, int NCH = 8>
 void run(int threads, int iters) {
-    auto k = issue_kernel<NV, NE, LDSPER, ROLE>;
+    auto k = issue_kernel<NV, NE, LDSPER, ROLE, NCH>;
     if (hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds) != hipSuccess) {
         std::printf("attribute failed\n");
         std::exit(1);
@@ -132,7 +133,7 @@ void run(int threads, int iters) {
     const double slots = (double)iters * 64;
     const double mfma_per_simd = slots * (ROLE == 0 ? nw / 4 : 1);
     const double flops = 32768.0 * mfma_per_simd * 4 * g_cus;
-    std::printf("%-5s NV=%2d NE=%d LDS every %d MFMA | waves/SIMD %d | MFMA-wave cycles per MFMA %6.2f", ROLE ? "split" : "mixed",
+    std::printf("%-5s chains %d NV=%2d NE=%d LDS every %d MFMA | waves/SIMD %d | MFMA-wave cycles per MFMA %6.2f", ROLE ? "split" : "mixed", NCH,
                 NV, NE, LDSPER, nw / 4, cm / slots);
     if (ROLE) std::printf(" | vector-wave cycles per slot %6.2f", cv / nv / slots);
     std::printf(" | %.0f TFLOP/s in %.2f ms\n", flops / (ms * 1e-3) / 1e12, ms);
@@ -147,8 +148,22 @@ int main(int argc, char **argv) {
         return 1;
     }
     (void)hipMemset(g_sink, 0, sizeof(float) * 2);
+    // The engine clock ramps up over the first tens of milliseconds of load:
+    // about half a second of MFMA work first, so that every row is timed at
+    // the loaded clock.
+    {
+        auto k = issue_kernel<0, 0, 0, 0, 8>;
+        if (hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds) != hipSuccess) {
+            std::printf("attribute failed\n");
+            return 1;
+        }
+        for (int i = 0; i < 50; ++i) hipLaunchKernelGGL(k, dim3(g_cus), dim3(256), kLds, 0, g_sink, 4000, g_cyc);
+        (void)hipDeviceSynchronize();
+    }
     std::printf("compute units %d, %d iterations x 64 MFMA slots per wave\n", g_cus, iters);
     run<0, 0, 0, 0>(256, iters);
+    run<0, 0, 0, 0, 2>(256, iters);
+    run<0, 0, 0, 0, 1>(256, iters);
     run<0, 0, 0, 0>(512, iters / 2);
     run<2, 0, 0, 0>(256, iters);
     run<4, 0, 0, 0>(256, iters);
