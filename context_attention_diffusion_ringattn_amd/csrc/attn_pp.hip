@@ -294,20 +294,38 @@ void attn_pp_kernel(const AttnArgs a) {
         // the row sum is taken over the float32 probabilities: with a peaked
         // softmax one term dominates it, and its bf16 rounding (2^-9
         // relative) would go straight into the LSE
+        // In chunks of eight independent scores: their eight fmas, then the
+        // eight exps, then the sums and the bf16 packing.  Left to itself
+        // the compiler pairs each fma with its exp through one temporary
+        // register, and the softmax wave (alone on its SIMD's vector unit in
+        // this phase) waits on every pair.
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p0 = fast_exp2(fmaf(s0[e], sl2, -mc));
-            const float p1 = fast_exp2(fmaf(s0[8 + e], sl2, -mc));
-            const float p2 = fast_exp2(fmaf(s1[e], sl2, -mc));
-            const float p3 = fast_exp2(fmaf(s1[8 + e], sl2, -mc));
-            l0 += p0;
-            l1 += p1;
-            l2 += p2;
-            l3 += p3;
-            pb[0][e] = (__bf16)p0;
-            pb[1][e] = (__bf16)p1;
-            pb[2][e] = (__bf16)p2;
-            pb[3][e] = (__bf16)p3;
+        for (int e0 = 0; e0 < 8; e0 += 2) {
+            float x[2][4];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                x[k][0] = fmaf(s0[e0 + k], sl2, -mc);
+                x[k][1] = fmaf(s0[8 + e0 + k], sl2, -mc);
+                x[k][2] = fmaf(s1[e0 + k], sl2, -mc);
+                x[k][3] = fmaf(s1[8 + e0 + k], sl2, -mc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[k][i] = fast_exp2(x[k][i]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                l0 += x[k][0];
+                l1 += x[k][1];
+                l2 += x[k][2];
+                l3 += x[k][3];
+                pb[0][e0 + k] = (__bf16)x[k][0];
+                pb[1][e0 + k] = (__bf16)x[k][1];
+                pb[2][e0 + k] = (__bf16)x[k][2];
+                pb[3][e0 + k] = (__bf16)x[k][3];
+            }
         }
     };
 
