@@ -187,8 +187,11 @@ void attn_w3_kernel(const AttnArgs a) {
     const float sl2 = a.scale_log2e;
     constexpr int kDsRead = 0x100, kMfma = 0x008;
 
-    // One tile in stage S: scores, online softmax, PV.
-    auto compute = [&](auto stage, int t) __attribute__((always_inline)) {
+    // One tile in stage S: scores, online softmax, PV.  on_max() runs once
+    // the row maxima are known: the step issues its tile loads there, where
+    // the wait for the load unit to take them overlaps the max chain's
+    // latency instead of holding up the step's first instructions.
+    auto compute = [&](auto stage, int t, auto &&on_max) __attribute__((always_inline)) {
         constexpr uint32_t S = decltype(stage)::value;
         constexpr uint32_t KS = S * G::TILE, VS = S * G::TILE;
         // S^T = K Q^T: one 32-key block, lane half h holds keys 16h + v
@@ -217,6 +220,7 @@ void attn_w3_kernel(const AttnArgs a) {
 #pragma unroll
         for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
         mx = fmaxf(mx, other_half(mx, half != 0));
+        on_max();
         if (__any(mx > m_run)) {  // wave-uniform; rare once the row maxima settle
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2((m_run - m_new) * sl2);
@@ -261,7 +265,7 @@ void attn_w3_kernel(const AttnArgs a) {
 
     // ---- sweep: step j is tile t_lo + KG j + kg of each key group, in stage
     // j % 3; loads issued two steps ahead ------------------------------------
-    // A group's step-j tile's loads are issued at the start of step j-2 (into
+    // A group's step-j tile's loads are issued during step j-2 (into
     // the stage that its step j-3 used, released by the barrier at the end of
     // step j-3) and waited for before the barrier at the end of step j-1,
     // which publishes them to the whole workgroup.  The groups step together;
@@ -278,9 +282,12 @@ void attn_w3_kernel(const AttnArgs a) {
     wg_barrier();
     auto step = [&](auto sc, auto sl, int j) __attribute__((always_inline)) -> bool {
         if (j >= Ts) return false;
-        if (j + 2 < Tg) issue_loads(sl, tile_of(j + 2));
+        auto loads = [&]() __attribute__((always_inline)) {
+            if (j + 2 < Tg) issue_loads(sl, tile_of(j + 2));
+        };
         __builtin_amdgcn_sched_barrier(0);
-        if (j < Tg) compute(sc, tile_of(j));
+        if (j < Tg) compute(sc, tile_of(j), loads);
+        else loads();
         __builtin_amdgcn_sched_barrier(0);
         if (j + 2 < Tg) wait_vmcnt<G::VM_PER_TILE>();
         else wait_vmcnt<0>();
