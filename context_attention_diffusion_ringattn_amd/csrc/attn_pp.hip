@@ -358,15 +358,14 @@ void attn_pp_kernel(const AttnArgs a) {
     // The softmax phase of step j, with the waits and barriers around it.
     // Each group issues its share of the loads of tile j+2 in its softmax
     // phase -- never in the MFMA phase, where a stalled vector-memory issue
-    // would idle the matrix pipe -- once the row maxima are known: the four
-    // waves of a group issue them together and each waits until the load
-    // unit takes its requests; at the very start of the phase that wait came
-    // before the first vector instruction, after the dependent max chain it
-    // overlaps that chain's latency (7.5 % fewer cycles per tile at D = 64,
-    // 1.5 % at D = 128).  Before the barrier
-    // that publishes tile j+1, group B (end of its MFMA phase) has no later
-    // loads in flight and waits for all; group A (end of its softmax phase)
-    // may leave the loads of tile j+2 in flight.
+    // would idle the matrix pipe.  The loads go out once the row maxima are
+    // known: the four waves of a group issue them together and each stalls
+    // until the load unit takes its requests, a stall that there overlaps
+    // the latency of the dependent max chain instead of delaying the phase's
+    // first vector instruction.  Before the barrier that publishes tile j+1,
+    // group B (end of its MFMA phase) has no later loads in flight and waits
+    // for all; group A (end of its softmax phase) may leave the loads of
+    // tile j+2 in flight.
     auto softmax_phase = [&](auto sl, int j) __attribute__((always_inline)) {
         if (grp == 1) wait_vmcnt<0>();
         wg_barrier();
