@@ -406,7 +406,7 @@ void attn_pp_kernel(const AttnArgs a) {
     // ---- epilogue -------------------------------------------------------------
     const float l_lane = (l0 + l1) + (l2 + l3);
     const float l_tot = l_lane + other_half(l_lane, half != 0);
-    if constexpr (D == 128 && (MODE == kModeFinal || MODE == kModePartial)) {
+    if constexpr (D == 128 && (MODE == kModeFinal || MODE == kModePartial || MODE == kModeAccum)) {
         // The K stages are free: the last QK phase ended before the barrier
         // both groups passed on their way here.  The V stages are not: waves
         // of the trailing group may still read V of the last tile, with no

@@ -264,9 +264,15 @@ __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[
 // against bank conflicts), then each store instruction covers eight rows of
 // 32 consecutive floats.  The LDS exchange stays inside the wave (LDS
 // operations of one wave complete in order), so every lane takes part and
-// only the global stores of rows at or past q_end are skipped.  `row0` is
+// only the global accesses of rows at or past q_end are skipped.  `row0` is
 // the wave's first query row, `scratch` an LDS byte address of
 // 32 * kStageRowFloats * 4 bytes that no other wave touches.
+// Accum (the ring step's in-place LSE merge into the float32 accumulator):
+// each lane works out its row's weights from the stored and the new LSE, as
+// write_rows does, scales its outputs by the new side's weight before
+// staging them, and leaves the stored side's weight (and whether the stored
+// LSE is -inf) in the row's padding words; the read-back lanes then read the
+// accumulator in the same whole row segments they write.
 constexpr int kStageRowFloats = 36;
 constexpr uint32_t kStageBytes = 32u * kStageRowFloats * 4u;
 
@@ -274,8 +280,10 @@ template <int D, int MODE>
 __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x16 (&o)[D / 32], float m_run,
                                                   float l_tot, bool any_keys, int b, int h, int64_t row0,
                                                   int64_t q_end, int split, int lane, uint32_t scratch) {
-    static_assert(MODE == kModeFinal || MODE == kModePartial, "stores only");
+    static_assert(MODE == kModeFinal || MODE == kModePartial || MODE == kModeAccum, "float32 modes");
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    typedef __attribute__((address_space(3))) float lds_f32;
+    if (MODE == kModeAccum && !any_keys) return;  // merging an empty partial changes nothing
     const int col = lane & 31, half = lane >> 5;
     const int64_t HD = (int64_t)a.heads * D;
     float *obase = a.out + ((int64_t)b * a.q_pitch + row0) * HD + (int64_t)h * D;
@@ -289,22 +297,53 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
     const int rr = lane >> 3;       // read-back row within a group of eight
     const int c4 = 4 * (lane & 7);  // read-back first column
     const int64_t rows_left = q_end - row0;
+    float w_self = inv_l;  // this lane's row: weight of the new partial's outputs
+    float wa_rd[4];        // read-back rows 8k + rr: weight of the stored side
+    bool copy_rd[4];       // ... and whether the stored LSE is -inf (copy, never multiply)
+    if constexpr (MODE == kModeAccum) {
+        const float la = col < rows_left ? *lptr : -INFINITY;
+        float wa = 0.f, wb = 1.f, lse_new = lse_chunk;
+        if (la != -INFINITY) {
+            lse_new = fmaxf(la, lse_chunk) + log1pf(expf(-fabsf(la - lse_chunk)));
+            wa = expf(la - lse_new);
+            wb = expf(lse_chunk - lse_new);
+        }
+        w_self = wb * inv_l;
+        if (half == 0) {
+            *(lds_f32 *)(uintptr_t)(scratch + (uint32_t)(col * kStageRowFloats + 32) * 4u) = wa;
+            *(lds_f32 *)(uintptr_t)(scratch + (uint32_t)(col * kStageRowFloats + 33) * 4u) =
+                la == -INFINITY ? 1.f : 0.f;
+            if (col < rows_left) *lptr = lse_new;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t rw = scratch + (uint32_t)((8 * k + rr) * kStageRowFloats) * 4u;
+            wa_rd[k] = *(lds_f32 *)(uintptr_t)(rw + 32 * 4u);
+            copy_rd[k] = *(lds_f32 *)(uintptr_t)(rw + 33 * 4u) != 0.f;
+        }
+    }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const uint32_t at = scratch + (uint32_t)(col * kStageRowFloats + 8 * g + 4 * half) * 4u;
             *(lds_f32x4 *)(uintptr_t)at =
-                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]} * inv_l;
+                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]} * w_self;
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int r = 8 * k + rr;
-            const f32x4 v = *(lds_f32x4 *)(uintptr_t)(scratch + (uint32_t)(r * kStageRowFloats + c4) * 4u);
-            if (r < rows_left) *(f32x4 *)(obase + (int64_t)r * HD + 32 * db + c4) = v;
+            f32x4 v = *(lds_f32x4 *)(uintptr_t)(scratch + (uint32_t)(r * kStageRowFloats + c4) * 4u);
+            if (r < rows_left) {
+                f32x4 *p = (f32x4 *)(obase + (int64_t)r * HD + 32 * db + c4);
+                if constexpr (MODE == kModeAccum) {
+                    if (!copy_rd[k]) v += wa_rd[k] * (*p);
+                }
+                *p = v;
+            }
         }
     }
-    if (half == 0 && col < rows_left) *lptr = lse_chunk;
+    if (MODE != kModeAccum && half == 0 && col < rows_left) *lptr = lse_chunk;
 }
 
 }  // namespace ringattn
