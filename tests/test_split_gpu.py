@@ -49,10 +49,14 @@ def check(out, lse, ref_out, ref_lse, what):
 
 
 @pytest.mark.parametrize("name", ["tiny", "flux", "ring_anything"])
-@pytest.mark.parametrize("splits,block_m", [(0, 0), (2, 256), (3, 256), (5, 128), (4, 128)])
+@pytest.mark.parametrize("splits,block_m", [(0, 0), (1, 256), (2, 256), (3, 256), (1, 128), (5, 128), (4, 128)])
 def test_split_step_ring_loop(ra, name, splits, block_m):
     """The ring's loop with ringattn_step_split: one workspace serves every
-    chunk; after the last chunk the accumulators hold the oracle's result."""
+    chunk; after the last chunk the accumulators hold the oracle's result.
+    One split of 256 rows is the 8-wave kernel's in-place LSE merge into the
+    accumulator (staged through LDS at D = 128), one of 128 rows the 4-wave
+    kernel's; with ragged query rows (Ring Anything: 577) and, for tiny,
+    D = 64."""
     x = inputs(name)
     w = x["workload"]
     print(f"case {name} splits={splits} block_m={block_m}", flush=True)
