@@ -4,7 +4,9 @@ Usage: ``python -m context_attention_diffusion_ringattn_amd.build``.  Every
 call compiles from source (hipcc cross-compiles; no GPU is needed).
 ``--sanitize`` builds a host-only AddressSanitizer + UndefinedBehaviorSanitizer
 copy under ``_build/sanitize``; ``--sanitize-test`` also runs the CPU tests
-against it.
+against it.  ``--cycles`` builds a measurement copy under ``_build/cycles``
+whose 8-wave kernel logs, per workgroup, the engine cycles and reference
+ticks of its sweep (read by ``probes/sweep_cycles.py``).
 """
 
 from __future__ import annotations
@@ -101,6 +103,32 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+CYCLES_DIR = os.path.join(BUILD_DIR, "cycles")
+CYCLES_LIB = os.path.join(CYCLES_DIR, "libringattn.so")
+
+
+def build_cycles(verbose: bool = False) -> str:
+    """The library with the 8-wave kernel's sweep cycle log compiled in
+    (RINGATTN_CYCLE_COUNTERS); the same kernels otherwise."""
+    hipcc = _hipcc()
+    os.makedirs(CYCLES_DIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(CYCLES_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc, *COMMON_FLAGS, "-DRINGATTN_CYCLE_COUNTERS", "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compiling {src} (cycle counters) failed:\n{res.stdout}{res.stderr}")
+        objs.append(obj)
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", CYCLES_LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking the cycle-counter library failed:\n{res.stdout}{res.stderr}")
+    return CYCLES_LIB
+
+
 SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
 SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libringattn.so")
 
@@ -177,6 +205,9 @@ def sanitize_test() -> int:
 if __name__ == "__main__":
     if "--sanitize-test" in sys.argv:
         sys.exit(sanitize_test())
+    if "--cycles" in sys.argv:
+        print(build_cycles(verbose="-v" in sys.argv))
+        sys.exit(0)
     if "--sanitize" in sys.argv:
         print(build_sanitized(verbose="-v" in sys.argv))
         sys.exit(0)

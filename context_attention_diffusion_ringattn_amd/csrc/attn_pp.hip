@@ -32,6 +32,19 @@
 
 #include <type_traits>
 
+#ifdef RINGATTN_CYCLE_COUNTERS
+// Measurement build only (build.py --cycles): per workgroup, the engine
+// cycles (s_memtime) and 100 MHz reference ticks (s_memrealtime) its first
+// wave spent in the sweep, between the barrier after the prologue and the
+// barrier before the epilogue, and the sweep's tile count.
+constexpr int kCycleSlots = 8192;
+__device__ unsigned long long ringattn_cycle_log[kCycleSlots * 4];
+extern "C" int ringattn_cycle_log_read(void *dst, size_t bytes) {
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(ringattn_cycle_log), bytes, 0, hipMemcpyDeviceToHost);
+}
+extern "C" int ringattn_cycle_log_slots() { return kCycleSlots; }
+#endif
+
 namespace ringattn {
 namespace {
 
@@ -353,6 +366,10 @@ void attn_pp_kernel(const AttnArgs a) {
     if (T > 1) issue_loads(I1, t_lo + 1);
     wait_vmcnt<0>();
     wg_barrier();
+#ifdef RINGATTN_CYCLE_COUNTERS
+    const unsigned long long cyc0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long ref0 = __builtin_amdgcn_s_memrealtime();
+#endif
     if (grp == 1) wg_barrier();
 
     // The softmax phase of step j, with the waits and barriers around it.
@@ -402,6 +419,18 @@ void attn_pp_kernel(const AttnArgs a) {
         if (!step(I3, j + 3)) break;
     }
     if (grp == 0) wg_barrier();  // both groups pass the same number of barriers
+#ifdef RINGATTN_CYCLE_COUNTERS
+    {
+        const unsigned long long cyc1 = __builtin_amdgcn_s_memtime();
+        const unsigned long long ref1 = __builtin_amdgcn_s_memrealtime();
+        if (tid == 0 && blockIdx.x < (unsigned)kCycleSlots) {
+            ringattn_cycle_log[blockIdx.x * 4 + 0] = cyc1 - cyc0;
+            ringattn_cycle_log[blockIdx.x * 4 + 1] = ref1 - ref0;
+            ringattn_cycle_log[blockIdx.x * 4 + 2] = (unsigned long long)T;
+            ringattn_cycle_log[blockIdx.x * 4 + 3] = 0;
+        }
+    }
+#endif
 
     // ---- epilogue -------------------------------------------------------------
     const float l_lane = (l0 + l1) + (l2 + l3);
