@@ -131,7 +131,7 @@ def _oracle_task(task):
 
 def oracle_workers() -> int:
     """Worker processes for the oracle: the host cores this process may run
-    on, at most 16 (a GPU machine's CPU share per GPU)."""
+    on, at most 16 (the host's CPU share per GPU)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
