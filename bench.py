@@ -54,6 +54,8 @@ def parse_args():
     ap.add_argument("--ring-steps", action="store_true",
                     help="time the ring's own loop on this shard instead of one forward call: accumulator "
                          "initialisation plus one split ring step (ringattn_step_split, library plan) per chunk")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (all of its launches) in a HIP graph once and time its replays")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the HBM byte "
                          "counters of a profiler run) and exit")
@@ -254,6 +256,21 @@ def main():
             ra.forward(q, k, v, chunk_offsets=offs, scale=x["scale"], n_splits=n_splits, block_m=block_m,
                        out=out, lse=lse, workspace=ws)
 
+    if args.graph:
+        # The library enqueues kernels on torch's current stream and nothing
+        # else, so a step captures as it is; one eager run on a side stream
+        # first, as capture requires.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        step = graph.replay
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -301,12 +318,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}_ring_sweep" if args.sweep else (f"{w.name}_ring_steps" if args.ring_steps
-                                                                    else w.name),
+            "workload": (f"{w.name}_ring_sweep" if args.sweep else (f"{w.name}_ring_steps" if args.ring_steps
+                                                                     else w.name)) + ("_graph" if args.graph else ""),
             "description": (f"every rank of the ring on one GPU ({w.n_chunks} ranks, rank-rotated chunk order, "
                             f"float32 merge per step); " if args.sweep else "")
                            + (f"the ring's loop: accumulator init + {w.n_chunks} split ring steps; "
-                              if args.ring_steps else "") + w.description,
+                              if args.ring_steps else "")
+                           + ("each step's launches replayed from one HIP graph; " if args.graph else "")
+                           + w.description,
             "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
             "q_rows": n_q, "kv_rows": w.seq_len, "n_chunks": w.n_chunks,
             "ring_anything": w.ring_anything,
