@@ -208,12 +208,15 @@ def test_ragged_shapes(ra, case):
                               block_m=block_m)
         torch.cuda.synchronize()
         assert_close(out, lse, ref_out, ref_lse, f"ragged padded block_m={block_m}")
-    out_acc, lse_acc = ra.new_accumulators(q)
-    for c in range(len(lens)):
-        ra.step(q, k[:, offs[c]:offs[c + 1]].contiguous(), v[:, offs[c]:offs[c + 1]].contiguous(),
-                out_acc, lse_acc, scale=x["scale"])
-    torch.cuda.synchronize()
-    assert_close(out_acc, lse_acc, ref_out, ref_lse, "ragged step path")
+    # the step path: the library's plan, then one split of 128 and of 256 rows
+    # (the 8-wave kernel's in-place merge, staged through LDS at D = 128)
+    for block_m in (0, 128, 256):
+        out_acc, lse_acc = ra.new_accumulators(q)
+        for c in range(len(lens)):
+            ra.step(q, k[:, offs[c]:offs[c + 1]].contiguous(), v[:, offs[c]:offs[c + 1]].contiguous(),
+                    out_acc, lse_acc, scale=x["scale"], n_splits=1, block_m=block_m)
+        torch.cuda.synchronize()
+        assert_close(out_acc, lse_acc, ref_out, ref_lse, f"ragged step path block_m={block_m}")
 
 
 def test_no_keys_gives_empty_result(ra):
