@@ -14,7 +14,8 @@
 //    phase (tile t).  While group A issues MFMAs, group B does its softmax on
 //    the VALU, and the other way round; workgroup barriers separate the
 //    phases and the MFMA phase runs at raised wave priority so the matrix
-//    pipe is fed first.
+//    pipe is fed first.  The MFMA phase is one software pipeline over both
+//    products, the LDS reads of the next four MFMAs always in flight.
 //  * K/V tiles stream through a ring of four LDS stages by direct
 //    global->LDS loads, issued two tiles ahead; each wave waits only for its
 //    own loads of the next tile before the barrier that publishes it.
@@ -211,59 +212,78 @@ void attn_pp_kernel(const AttnArgs a) {
     const float sl2 = a.scale_log2e;
 
     // The MFMA phase: O^T += V^T P^T for the previous tile (V in stage sv)
-    // and S^T = K Q^T for the current one (K in stage sk), as one straight
-    // run of MFMAs.  PV step st covers keys 32*(st>>1) + 16*half + 8*(st&1)
-    // + 0..7; QK uses two 32-key blocks whose accumulation chains interleave.
-    // Each half is scheduled to keep the LDS reads of its next kWin MFMAs
-    // in flight: 2 transposing reads per PV MFMA, 1 read per QK MFMA.
-    auto mfma_phase = [&](auto sv, auto sk, auto do_pv, auto do_qk) __attribute__((always_inline)) {
-        constexpr bool PV = decltype(do_pv)::value;
-        constexpr bool QK = decltype(do_qk)::value;
-        constexpr int kDsRead = 0x100, kMfma = 0x008, kWin = 4;
-        if constexpr (PV) {
-            constexpr uint32_t VS = decltype(sv)::value * G::TILE;
+    // and S^T = K Q^T for the current one (K in stage sk), as one software
+    // pipeline over its MFMAs, numbered m = 0 .. NPV+NQK-1.  m < NPV: PV
+    // step st = m / (D/32) (keys 32*(st>>1) + 16*half + 8*(st&1) + 0..7)
+    // for output block db = m % (D/32), A operand V^T from two transposing
+    // reads.  m >= NPV: QK step (m-NPV)/2 for key block (m-NPV)%2, A operand
+    // K from one 16-byte read; the two key blocks' chains interleave.  The A
+    // operand of MFMA m sits in ring[m % kRing], and MFMA m is followed by
+    // the reads for MFMA m + kRing, so kRing MFMAs' reads stay in flight and
+    // the reads of the first QK operands go out under the last PV MFMAs.
+    // A scheduling fence after each MFMA and its reads keeps this order.
+    constexpr int NPV = 4 * (D / 32);
+    constexpr int NQK = 2 * (D / 16);
+    constexpr int kRing = 4;
+    static_assert(NPV % kRing == 0 && NQK >= kRing, "ring slots line up across the two products");
+    bf16x8 ring[kRing];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int jrow = 32 * (st >> 1) + 8 * (st & 1);
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const s16x4 lo = lds_tr_at(vb[db], VS + jrow * G::ROW);
-                    const s16x4 hi = lds_tr_at(vb[db], VS + (jrow + 4) * G::ROW);
-                    const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[st], o[db], 0,
-                                                                     0, 0);
-                }
-            }
-            // keep the reads of the next kWin MFMAs in flight
-            constexpr int NPV = 4 * (D / 32);
-            __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * kWin, 0);
-#pragma unroll
-            for (int i = 0; i < NPV - kWin; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(kMfma, kWin, 0);
-            if constexpr (QK) __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < kRing; ++i) ring[i] = bf16x8{};
+    auto read_op = [&](int m, uint32_t VS, uint32_t KS) __attribute__((always_inline)) -> bf16x8 {
+        if (m < NPV) {
+            const int st = m / (D / 32), db = m % (D / 32);
+            const int jrow = 32 * (st >> 1) + 8 * (st & 1);
+            const s16x4 lo = lds_tr_at(vb[db], VS + jrow * G::ROW);
+            const s16x4 hi = lds_tr_at(vb[db], VS + (jrow + 4) * G::ROW);
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
-        if constexpr (QK) {
-            constexpr uint32_t KS = decltype(sk)::value * G::TILE;
-            s0 = f32x16{};
-            s1 = f32x16{};
+        const int q = m - NPV;
+        return lds_b128_at(kb[q >> 1], KS + (q & 1) * 32 * G::ROW);
+    };
+    auto mfma_at = [&](int m) __attribute__((always_inline)) {
+        const bf16x8 op = ring[m % kRing];
+        if (m < NPV) {
+            const int st = m / (D / 32), db = m % (D / 32);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pb[st], o[db], 0, 0, 0);
+        } else {
+            const int q = m - NPV;
+            if (q & 1) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[q >> 1], s1, 0, 0, 0);
+            else s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[q >> 1], s0, 0, 0, 0);
+        }
+    };
+    // PV of the tile in stage sv.  Its last kRing MFMAs carry the reads of
+    // the first QK operands (K in stage sk) whether or not a QK follows:
+    // keeping the PV code on one path keeps the output accumulators in the
+    // same registers on every step.
+    auto pv_pipe = [&](auto sv, auto sk) __attribute__((always_inline)) {
+        constexpr uint32_t VS = decltype(sv)::value * G::TILE;
+        constexpr uint32_t KS = decltype(sk)::value * G::TILE;
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                const bf16x8 k0 = lds_b128_at(kb[st], KS);
-                const bf16x8 k1 = lds_b128_at(kb[st], KS + 32 * G::ROW);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[st], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[st], s1, 0, 0, 0);
-            }
-            constexpr int NQK = 2 * (D / 16);
-            __builtin_amdgcn_sched_group_barrier(kDsRead, kWin, 1);
+        for (int m = 0; m < kRing; ++m) ring[m] = read_op(m, VS, KS);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < NQK - kWin; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
-            }
-            __builtin_amdgcn_sched_group_barrier(kMfma, kWin, 1);
+        for (int m = 0; m < NPV; ++m) {
+            mfma_at(m);
+            ring[m % kRing] = read_op(m + kRing, VS, KS);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // QK of the tile in stage sk; `first`: no PV precedes it in this phase,
+    // so it reads its own first operands.
+    auto qk_pipe = [&](auto sk, auto first) __attribute__((always_inline)) {
+        constexpr uint32_t KS = decltype(sk)::value * G::TILE;
+        if constexpr (decltype(first)::value) {
+#pragma unroll
+            for (int m = NPV; m < NPV + kRing; ++m) ring[m % kRing] = read_op(m, 0, KS);
+        }
+        s0 = f32x16{};
+        s1 = f32x16{};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = NPV; m < NPV + NQK; ++m) {
+            mfma_at(m);
+            if (m + kRing < NPV + NQK) ring[m % kRing] = read_op(m + kRing, 0, KS);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -360,8 +380,8 @@ void attn_pp_kernel(const AttnArgs a) {
     constexpr std::integral_constant<int, 1> I1{};
     constexpr std::integral_constant<int, 2> I2{};
     constexpr std::integral_constant<int, 3> I3{};
-    constexpr std::true_type ON{};
-    constexpr std::false_type OFF{};
+    constexpr std::true_type FIRST{};
+    constexpr std::false_type AFTER_PV{};
     if (T > 0) issue_loads(I0, t_lo);
     if (T > 1) issue_loads(I1, t_lo + 1);
     wait_vmcnt<0>();
@@ -395,8 +415,8 @@ void attn_pp_kernel(const AttnArgs a) {
         }
         wg_barrier();
     };
-    // Step j (j % 4 == J): the MFMA phase -- PV of tile j-1 (j >= 1) and QK
-    // of tile j (j < T) -- then, for j < T, the softmax phase of tile j.
+    // Step j >= 1 (j % 4 == J): the MFMA phase -- PV of tile j-1, then for
+    // j < T the QK of tile j -- then, for j < T, the softmax phase of tile j.
     auto step = [&](auto jc, int j) __attribute__((always_inline)) -> bool {
         constexpr int J = decltype(jc)::value;
         constexpr std::integral_constant<int, J> SK{};
@@ -404,19 +424,28 @@ void attn_pp_kernel(const AttnArgs a) {
         constexpr std::integral_constant<int, (J + 2) % 4> SL{};
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
-        if (j >= 1) mfma_phase(SV, SK, ON, OFF);
-        if (j < T) mfma_phase(SV, SK, OFF, ON);
+        pv_pipe(SV, SK);
+        if (j < T) qk_pipe(SK, AFTER_PV);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (j >= T) return false;
         softmax_phase(SL, j);
         return true;
     };
-    for (int j = 0;; j += 4) {  // unrolled by four so that every stage index is a constant
-        if (!step(I0, j)) break;
-        if (!step(I1, j + 1)) break;
-        if (!step(I2, j + 2)) break;
-        if (!step(I3, j + 3)) break;
+    if (T > 0) {
+        // step 0: the QK of tile 0 alone, then its softmax phase
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        qk_pipe(I0, FIRST);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        softmax_phase(I2, 0);
+        for (int j = 1;; j += 4) {  // unrolled by four so that every stage index is a constant
+            if (!step(I1, j)) break;
+            if (!step(I2, j + 1)) break;
+            if (!step(I3, j + 2)) break;
+            if (!step(I0, j + 3)) break;
+        }
     }
     if (grp == 0) wg_barrier();  // both groups pass the same number of barriers
 #ifdef RINGATTN_CYCLE_COUNTERS
@@ -437,10 +466,13 @@ void attn_pp_kernel(const AttnArgs a) {
     const float l_tot = l_lane + other_half(l_lane, half != 0);
     if constexpr (D == 128 && (MODE == kModeFinal || MODE == kModePartial || MODE == kModeAccum)) {
         // The K stages are free: the last QK phase ended before the barrier
-        // both groups passed on their way here.  The V stages are not: waves
-        // of the trailing group may still read V of the last tile, with no
-        // barrier after it.  At D = 64 the K stages cannot hold the slices of
-        // all eight waves, so that head dim keeps the direct stores.
+        // both groups passed on their way here.  (The trailing group's last
+        // MFMA phase still reads the first K operands of a QK that does not
+        // run; those values feed no MFMA, so what they read does not matter.)
+        // The V stages are not: waves of the trailing group may still read V
+        // of the last tile, with no barrier after it.  At D = 64 the K stages
+        // cannot hold the slices of all eight waves, so that head dim keeps
+        // the direct stores.
         static_assert(kPPWaves * kStageBytes <= 4 * G::TILE, "staging fits the K stages");
         write_rows_staged<D, MODE>(a, o, m_run, l_tot, T > 0, b, h, qrow - col, q_end, split, lane,
                                    lds0 + kKRegion + (uint32_t)wave * kStageBytes);
